@@ -1,0 +1,95 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies the oracle's C source, plants one mistake by text
+substitution, compiles the copy (on the CPU) and runs every pin of
+test_oracle.py against it; at least one pin must fail.  The committed oracle
+itself is never changed."""
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import test_oracle as P
+
+MUTANTS = [
+    ("nibbles swapped",
+     "(j < 16) ? (byte & 0xF) : (byte >> 4)", "(j < 16) ? (byte >> 4) : (byte & 0xF)"),
+    ("Q4 offset 8 dropped", "return nib - 8;", "return nib;"),
+    ("Q8 read unsigned", "(int)(int8_t)img[r * cols + c]", "(int)img[r * cols + c]"),
+    ("Q8 row stride wrong", "(int)(int8_t)img[r * cols + c]", "(int)(int8_t)img[r * 32 + c]"),
+    ("scales in column-major block order",
+     "r * (cols / 32) + c / 32);\n                double w",
+     "(c / 32) * rows + r);\n                double w"),
+    ("padding to 32", "((n + 63) / 64) * 64", "((n + 31) / 32) * 32"),
+    ("f16 exponent bias", "e - 25", "e - 24"),
+    ("f16 subnormal scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("-128 not rejected", "if (img[i] == 0x80) return ORC_FORMAT;", "(void)0;"),
+    ("norm without absolute values", "nrm += fabs(w) * fabs(a);", "nrm += w * a;"),
+    ("quantizer divides last",
+     "volatile float t = xb[j] * id;", "volatile float t = (xb[j] * 127.0f) / amax;"),
+    ("quantizer rounds half to even",
+     "float tr = truncf(u);", "float tr = rintf(t);"),
+    ("quantizer threshold", "if (amax < 1e-30f)", "if (amax <= 0.0f)"),
+    ("quantizer scale 1/128", "d[b] = amax / 127.0f;", "d[b] = amax / 128.0f;"),
+    ("bf16 widened wrongly", "(uint32_t)b << 16", "(uint32_t)b << 15"),
+    ("dequantized subnormals flushed",
+     "float w = (float)v * d;",
+     "float w = (float)v * d; if (fabsf(w) < 1.17549435e-38f) w = 0.0f;"),
+    ("shared classifier ignored",
+     "if (shared_classifier && (class_bit == 1 || class_bit == 2)) bits = 1u | 2u;",
+     "(void)shared_classifier;"),
+    ("block dot over 31 elements", "for (uint64_t j = 0; j < 32; ++j) {\n                acc +=",
+     "for (uint64_t j = 0; j < 31; ++j) {\n                acc +="),
+    ("limit 2^24 not enforced",
+     "if (rows > ORC_DIM_LIMIT || cols > ORC_DIM_LIMIT) return ORC_SHAPE;", ""),
+]
+
+
+def _pins():
+    out = []
+    for n in P.FIXTURES_W:
+        out.append((P.test_fixture_dequantized_values, (n,)))
+    for n in P.FIXTURES_Y:
+        out.append((P.test_fixture_products, (n,)))
+    out += [(P.test_fixture_product_bf16_activations, ()),
+            (P.test_quantizer_fixture, ()),
+            (P.test_quantizer_properties, ()),
+            (P.test_sizes_printed_on_pages, ()),
+            (P.test_rejects_fixture, ()),
+            (P.test_class_rule_hand_cases, ()),
+            (P.test_block_dots_hand_and_brute_force, ()),
+            (P.test_product_invariants, ())]
+    for wt, sf in [(1, 0), (2, 1)]:
+        out.append((P.test_product_exact_rational_brute_force, (wt, sf)))
+    return out
+
+
+def test_f16_decoder_mutant_fails_exhaustive_check(tmp_path, monkeypatch):
+    _install(tmp_path, monkeypatch, "e - 25", "e - 24")
+    with pytest.raises(AssertionError):
+        P.test_f16_decoder_exhaustive_against_numpy()
+
+
+def _install(tmp_path, monkeypatch, old, new):
+    src = open(O._SRC).read()
+    assert src.count(old) >= 1, old
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC",
+                           "-shared", "-o", str(so), str(path), "-lm"])
+    monkeypatch.setattr(O, "_lib", None)
+    monkeypatch.setattr(O, "_LIB_PATH", str(so))
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    _install(tmp_path, monkeypatch, old, new)
+    failed = []
+    for fn, args in _pins():
+        try:
+            fn(*args)
+        except Exception as e:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(fn.__name__)
+    assert failed, f"no pin catches: {name}"
