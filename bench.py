@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Throughput of the block-quantized weight x activation product on one
+MI355X, printed as one JSON line.
+
+A step is one pass of the product over one batch of synthetic input (seeded,
+block_quant_weight_amd.synth).  The weights of successive steps rotate over
+enough byte-identical copies (>= 512 MB in total) that neither the 256 MB
+MALL nor the L2 can serve them: every step reads its weights from HBM.  The
+timed steps run as one captured HIP graph (launch overhead out of the way),
+bracketed by device synchronisation and HIP events on the launching stream.
+
+Default workload: Q4_0 GEMV, 4096 x 4096, f16 scales, batch 1.  Other
+workloads (--workload): q8_gemv_512, decode_layer, gemm_q4_14336x4096,
+gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, and copy (a plain
+device copy, used to calibrate HBM byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Q4_0/Q8_0 GEMV effective GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+Q8, Q4 = 1, 2
+ROTATE_BYTES = 512 << 20
+
+LAYER = [("wq", 4, 4096, 4096), ("wk", 4, 1024, 4096), ("wv", 8, 1024, 4096),
+         ("wo", 16, 4096, 4096), ("w1", 32, 11008, 4096), ("w3", 32, 11008, 4096),
+         ("w2", 64, 4096, 11008)]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload(name):
+    """(description, kind, config id, [(matrix id, wtype, scale_f16, rows, cols)], batch)."""
+    from block_quant_weight_amd import qmv as Q
+    if name == "q4_gemv_4096":
+        return ("Q4_0 GEMV 4096x4096, f16 scales, batch 1", "gemv", 2,
+                [(0, Q4, 1, 4096, 4096)], 1)
+    if name == "q8_gemv_512":
+        return ("Q8_0 GEMV 512x512, f32 scales, batch 1", "gemv", 1,
+                [(0, Q8, 0, 512, 512)], 1)
+    if name == "decode_layer":
+        mats = []
+        for m, (_, cls, r, c) in enumerate(LAYER):
+            mats.append((m, Q.qmv_class_wtype(Q4, 8 | 64, cls, 0), 1, r, c))
+        return ("mixed decode layer (q8_mask 8|64: wv, w2 Q8_0; others Q4_0), "
+                "dim 4096, kv 1024, ffn 11008, f16 scales, batch 1", "gemv", 3, mats, 1)
+    if name == "gemm_q4_14336x4096":
+        return ("prefill GEMM Q4_0 14336x4096 f16 scales x bf16 [512x4096]", "gemm", 4,
+                [(0, Q4, 1, 14336, 4096)], 512)
+    if name == "gemm_q8_4096x14336":
+        return ("prefill GEMM Q8_0 4096x14336 f32 scales x bf16 [512x14336]", "gemm", 4,
+                [(1, Q8, 0, 4096, 14336)], 512)
+    if name in ("lm_head_b1", "lm_head_b64"):
+        b = 1 if name.endswith("b1") else 64
+        return (f"shared-classifier LM head Q8_0 248320x1024 f16 scales, f32 hidden, "
+                f"batch {b}", "gemv", 5, [(0, Q8, 1, 248320, 1024)], b)
+    if name == "embed_64":
+        return ("embedding gather of 64 ids from Q8_0 248320x1024 f16 scales", "embed", 5,
+                [(0, Q8, 1, 248320, 1024)], 64)
+    if name == "copy":
+        return ("plain device copy of 256 MiB (counter calibration)", "copy", 0, [], 0)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def matrix_bytes(wt, sf, r, c):
+    q = r * c if wt == Q8 else r * c // 2
+    return q + (r * c // 32) * (2 if sf else 4)
+
+
+def step_work(kind, mats, batch):
+    """Algorithmic bytes and flops of one step."""
+    byts = flops = 0
+    for _, wt, sf, r, c in mats:
+        w = matrix_bytes(wt, sf, r, c)
+        if kind == "gemv":
+            byts += w + 4 * c * batch + 4 * r * batch
+            flops += 2 * r * c * batch
+        elif kind == "gemm":
+            byts += w + 2 * c * batch + 4 * r * batch
+            flops += 2 * r * c * batch
+        elif kind == "embed":
+            byts += batch * (matrix_bytes(wt, sf, 1, c)) + 4 * batch + 4 * batch * c
+    return byts, flops
+
+
+def make_image(config, m, wt, sf, r, c):
+    from block_quant_weight_amd import qmv as Q
+    from block_quant_weight_amd import synth
+    gq = synth.rng(config, m, synth.STREAM_QUANTS)
+    gd = synth.rng(config, m, synth.STREAM_SCALES)
+    q = synth.q8_quants(gq, r, c) if wt == Q8 else synth.q4_quants(gq, r, c)
+    d = synth.scales(gd, r * c // 32, bool(sf))
+    sp = Q.qmv_span(wt, sf, r, c)
+    img = np.zeros(sp["min_span"], dtype=np.uint8)
+    img[:sp["q_bytes"]] = q.view(np.uint8)
+    img[sp["d_offset"]:] = d.view(np.uint8)
+    return img
+
+
+def kernel_source_hash(kind):
+    f = {"gemv": "gemv.hip", "gemm": "gemm.hip", "embed": "misc.hip"}.get(kind)
+    if f is None:
+        return None
+    with open(os.path.join(ROOT, "block_quant_weight_amd", "csrc", f), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(name, kind):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel source as it stands."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+        if t.get("kernel_source_sha256_16") != kernel_source_hash(kind):
+            return None
+        return t.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(kind, config, mats, batch, budget_s):
+    """The oracle, as it stands, on this host's cores over a bounded sample."""
+    import oracle as O
+    from block_quant_weight_amd import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    m, wt, sf, r, c = mats[0]
+    img = make_image(config, m, wt, sf, r, c)
+    if kind == "embed":
+        ids = synth.token_ids(synth.rng(config, 0, synth.STREAM_IDS), batch, 3, r - 1)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < budget_s and reps < 100000:
+            O.dequant_rows(img, wt, sf, r, c, ids.astype(np.int64))
+            reps += 1
+        el = time.perf_counter() - t0
+        b, _ = step_work(kind, mats[:1], batch)
+        return {"value": reps * b / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{reps} gathers of {batch} rows, single thread"}
+    if kind == "gemm":
+        x = synth.act_bf16(synth.rng(config, m, synth.STREAM_ACT), batch, c)
+    else:
+        x = synth.act_f32(synth.rng(config, m, synth.STREAM_ACT), batch, c)
+    # rows per sample sized for about budget_s of work
+    probe = np.arange(min(r, 16), dtype=np.int64)
+    t0 = time.perf_counter()
+    O.product(img, wt, sf, r, c, x, sel=probe, threads=1)
+    per_row = max((time.perf_counter() - t0) / probe.size, 1e-7)
+    n_rows = int(min(r, max(threads, budget_s * threads / per_row)))
+    sel = np.linspace(0, r - 1, n_rows).astype(np.int64)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.product(img, wt, sf, r, c, x, sel=sel, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 0.5 * budget_s or reps >= 1000:
+            break
+    frac = reps * n_rows / r
+    if kind == "gemm":
+        flops = 2 * reps * n_rows * c * batch
+        return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"{reps} x {n_rows} of {r} rows x {batch} tokens "
+                          f"(f64, {threads} threads, {el:.1f} s)"}
+    byts, _ = step_work(kind, [mats[0]], batch)
+    return {"value": byts * frac / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} x {n_rows} of {r} rows of matrix 0, batch {batch} "
+                      f"(f64, {threads} threads, {el:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="q4_gemv_4096")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the product runs on a single MI355X; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_quant_weight_amd import qmv as Q
+    from block_quant_weight_amd import synth
+
+    desc, kind, config, mats, batch = workload(args.workload)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    if kind == "copy":
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n,
+                          "ms_per_copy": ms, "GB/s": 2 * n / ms / 1e6}))
+        return
+
+    step_bytes, step_flops = step_work(kind, mats, batch)
+    set_bytes = sum(matrix_bytes(wt, sf, r, c) for _, wt, sf, r, c in mats)
+    ncopies = max(2, -(-ROTATE_BYTES // set_bytes))
+    if kind == "embed":
+        ncopies = 1   # a gather touches 64 rows; rows are drawn afresh per step
+    steps = args.steps if args.steps is not None else (200 if kind == "gemm" else 1000)
+    warmup = args.warmup if args.warmup is not None else 20
+    log(f"workload {args.workload}: {desc}; {ncopies} weight copies; "
+        f"{steps} steps after {warmup} warm-up")
+
+    imgs = {m: make_image(config, m, wt, sf, r, c) for (m, wt, sf, r, c) in mats}
+    handles = []
+    for _ in range(ncopies):
+        hs = []
+        for (m, wt, sf, r, c) in mats:
+            h = Q.qmv_create(wt, sf, r, c)
+            Q.qmv_upload(h, imgs[m], stream=stream)
+            hs.append(h)
+        handles.append(hs)
+    del imgs
+    log("weights uploaded")
+
+    xs, ys = [], []
+    for (m, wt, sf, r, c) in mats:
+        g = synth.rng(config, m, synth.STREAM_ACT)
+        if kind == "gemm":
+            xb = synth.act_bf16(g, batch, c)
+            xs.append(torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16))
+        elif kind == "gemv":
+            xs.append(torch.from_numpy(synth.act_f32(g, batch, c)).cuda())
+        ys.append(torch.empty((batch, r), dtype=torch.float32, device="cuda"))
+    id_sets = []
+    if kind == "embed":
+        r = mats[0][3]
+        for k in range(64):
+            ids = synth.token_ids(synth.rng(config, k, synth.STREAM_IDS), batch, 3, r - 1)
+            id_sets.append(torch.from_numpy(ids).cuda())
+        out = torch.empty((batch, mats[0][4]), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        hs = handles[i % ncopies]
+        for j, h in enumerate(hs):
+            if kind == "gemv":
+                Q.qmv_gemv(h, xs[j], ys[j])
+            elif kind == "gemm":
+                Q.qmv_gemm(h, xs[j], ys[j])
+            else:
+                Q.qmv_embed_rows(h, id_sets[i % len(id_sets)], out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(warmup + i)
+        g.replay()                        # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+    log("warm-up done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    if use_graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_step = ms / steps
+    log(f"timed {steps} steps: {ms:.3f} ms")
+
+    launches_per_step = len(mats)
+    if kind == "gemm":
+        value, unit = step_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        bound, peak, runit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved = value
+        dtype = "bf16"
+    else:
+        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        bound, peak, runit = "hbm", HBM_PEAK_GBS, "GB/s"
+        achieved = value
+        dtype = "f32"
+    traffic = traffic_from_profiles(args.workload, "gemm" if (kind == "gemv" and batch > 8)
+                                    else kind)
+    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": {"gemv": "gemv_kernel" if batch <= 8 else "gemm_kernel (f32 split)",
+                       "gemm": "gemm_kernel", "embed": "embed_kernel"}[kind],
+            "launches_per_step": launches_per_step,
+            "algorithmic_bytes_per_step": step_bytes, "flops_per_step": step_flops}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline(kind, config, mats, batch, args.cpu_budget)
+    for hs in handles:
+        for h in hs:
+            Q.qmv_destroy(h)
+    wl = {"workload": args.workload, "description": desc, "batch": batch,
+          "matrices": [{"wtype": "Q8_0" if wt == Q8 else "Q4_0",
+                        "scales": "f16" if sf else "f32", "rows": r, "cols": c}
+                       for _, wt, sf, r, c in mats],
+          "weight_copies_rotated": ncopies, "hip_graph": use_graph}
+    print(json.dumps({
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded; uniform quants and scales, N(0,1) "
+                                "activations)",
+        "config": wl, "roofline": roof, "cpu_baseline": cpu}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

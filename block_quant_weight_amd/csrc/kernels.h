@@ -1,0 +1,37 @@
+// Launchers of the gfx950 kernels (internal to libqmv).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace qmv {
+
+// A device-resident matrix: q array at `q`, scales at `d` (f16 or f32).
+struct MatView {
+    const uint8_t* q;
+    const void* d;
+    uint32_t wtype, scale_f16, rows, cols;
+};
+
+// y[t][r] = sum_c W[r][c] x[t][c]; x f32 [batch][cols], y f32 [batch][rows].
+hipError_t launch_gemv(const MatView& m, const float* x, float* y,
+                       uint32_t batch, hipStream_t stream);
+
+// Same product on the matrix cores: x is bf16 bits, or f32 split into two
+// bf16 terms (x_f32 = true).
+hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
+                       uint32_t batch, hipStream_t stream);
+
+// out[i][c] = fl32(v * d) of row ids[i] (zeros for an id out of range).
+hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,
+                        float* out, hipStream_t stream);
+
+// Activation Q8_0 quantizer over n floats (n % 32 == 0).
+hipError_t launch_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,
+                              hipStream_t stream);
+
+// s[r][b] = sum_j v[r][32b+j] * xq[32b+j] (int32).
+hipError_t launch_block_dots(const MatView& m, const int8_t* xq, int32_t* s,
+                             hipStream_t stream);
+
+}  // namespace qmv

@@ -1,0 +1,134 @@
+// Host-side rules of the qmv library that need no GPU: array sizes, the
+// q8_mask class rule, the checks applied to a matrix's bytes, status text.
+// This translation unit makes no HIP call, so these rules can be exercised
+// on a machine without a GPU.
+//
+// Source: Krafla, ".mlb model, version 1" format page - "Body" (the
+// two-array quantized matrix, 64-byte padding), "Q8_0" (no -128 quant), the
+// q8_mask paragraph, and "Validation done by the loader" (error classes,
+// overflow-checked size arithmetic).
+#include <cstddef>
+#include <cstdint>
+
+#include "qmv.h"
+#include "qmv_layout.h"
+
+namespace qmv {
+
+namespace {
+constexpr uint64_t kDimLimit = uint64_t{1} << 24;
+
+// a + b and a * b with overflow detection (u64).
+bool add_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    return !__builtin_add_overflow(a, b, out);
+}
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
+    return !__builtin_mul_overflow(a, b, out);
+}
+bool round_up64(uint64_t n, uint64_t* out) {
+    uint64_t t;
+    if (!add_ok(n, 63, &t)) return false;
+    *out = t & ~uint64_t{63};
+    return true;
+}
+}  // namespace
+
+int compute_layout(uint32_t wtype, uint32_t scale_f16, uint32_t rows,
+                   uint32_t cols, Layout* L) {
+    if (wtype != QMV_Q8_0 && wtype != QMV_Q4_0) return QMV_E_FORMAT;
+    if (scale_f16 > 1) return QMV_E_FORMAT;
+    if (rows == 0 || cols == 0 || (cols & 31) != 0) return QMV_E_SHAPE;
+    if (rows > kDimLimit || cols > kDimLimit) return QMV_E_SHAPE;
+    uint64_t elems, q_bytes, d_bytes, d_off, min_span, d_pad, full;
+    if (!mul_ok(rows, cols, &elems)) return QMV_E_SHAPE;
+    q_bytes = (wtype == QMV_Q8_0) ? elems : elems / 2;
+    if (!mul_ok(elems / 32, scale_f16 ? 2 : 4, &d_bytes)) return QMV_E_SHAPE;
+    if (!round_up64(q_bytes, &d_off)) return QMV_E_SHAPE;
+    if (!add_ok(d_off, d_bytes, &min_span)) return QMV_E_SHAPE;
+    if (!round_up64(d_bytes, &d_pad) || !add_ok(d_off, d_pad, &full))
+        return QMV_E_SHAPE;
+    L->wtype = wtype;
+    L->scale_f16 = scale_f16;
+    L->rows = rows;
+    L->cols = cols;
+    L->q_bytes = q_bytes;
+    L->d_offset = d_off;
+    L->d_bytes = d_bytes;
+    L->min_span = min_span;
+    L->full_span = full;
+    return QMV_OK;
+}
+
+int check_bytes(const Layout& L, const void* src, uint64_t nbytes) {
+    if (src == nullptr) return QMV_E_ARG;
+    if (nbytes < L.min_span) return QMV_E_FORMAT;
+    if (L.wtype == QMV_Q8_0) {
+        // A Q8_0 quant of -128 (byte 0x80) is refused; the scan reads the q
+        // array eight bytes at a time.
+        const uint8_t* p = static_cast<const uint8_t*>(src);
+        uint64_t i = 0;
+        for (; i + 8 <= L.q_bytes; i += 8) {
+            uint64_t w;
+            __builtin_memcpy(&w, p + i, 8);
+            // a byte equals 0x80 iff (b ^ 0x80) == 0: classic zero-byte test
+            uint64_t v = w ^ 0x8080808080808080ull;
+            if ((v - 0x0101010101010101ull) & ~v & 0x8080808080808080ull) {
+                for (uint64_t j = i; j < i + 8; ++j)
+                    if (p[j] == 0x80) return QMV_E_FORMAT;
+            }
+        }
+        for (; i < L.q_bytes; ++i)
+            if (p[i] == 0x80) return QMV_E_FORMAT;
+    }
+    return QMV_OK;
+}
+
+}  // namespace qmv
+
+extern "C" {
+
+int qmv_span(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
+             uint64_t* q_bytes, uint64_t* d_offset, uint64_t* d_bytes,
+             uint64_t* min_span) {
+    qmv::Layout L;
+    int st = qmv::compute_layout(wtype, scale_f16, rows, cols, &L);
+    if (st != QMV_OK) return st;
+    if (q_bytes) *q_bytes = L.q_bytes;
+    if (d_offset) *d_offset = L.d_offset;
+    if (d_bytes) *d_bytes = L.d_bytes;
+    if (min_span) *min_span = L.min_span;
+    return QMV_OK;
+}
+
+int qmv_class_wtype(uint32_t file_wtype, uint32_t q8_mask, uint32_t class_bit,
+                    uint32_t shared_classifier, uint32_t* wtype_out) {
+    if (wtype_out == nullptr) return QMV_E_ARG;
+    if (file_wtype != QMV_Q8_0 && file_wtype != QMV_Q4_0) return QMV_E_FORMAT;
+    // exactly one of the seven class bits
+    if (class_bit == 0 || class_bit > 64 || (class_bit & (class_bit - 1)) != 0)
+        return QMV_E_ARG;
+    if (file_wtype == QMV_Q8_0) {
+        *wtype_out = QMV_Q8_0;
+        return QMV_OK;
+    }
+    uint32_t mask_bits = class_bit;
+    // With a shared classifier the embedding matrix is the classifier too:
+    // either of its two class bits selects Q8_0 for it.
+    if (shared_classifier != 0 && class_bit <= 2) mask_bits = 3;
+    *wtype_out = (q8_mask & mask_bits) ? QMV_Q8_0 : QMV_Q4_0;
+    return QMV_OK;
+}
+
+const char* qmv_status_str(int status) {
+    switch (status) {
+        case QMV_OK: return "ok";
+        case QMV_E_ARG: return "invalid argument";
+        case QMV_E_FORMAT: return "bad matrix format or bytes";
+        case QMV_E_SHAPE: return "bad matrix shape";
+        case QMV_E_DEVICE: return "HIP runtime error";
+        case QMV_E_NOMEM: return "out of memory";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

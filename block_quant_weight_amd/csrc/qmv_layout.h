@@ -1,0 +1,23 @@
+// Shape and byte layout of one quantized matrix (no HIP types).
+#pragma once
+#include <cstdint>
+
+namespace qmv {
+
+// The two arrays of a quantized matrix as the .mlb format lays them out:
+// q (quants) at byte 0, d (one scale per 32 weights) at d_offset =
+// pad64(q_bytes); min_span = d_offset + d_bytes, full_span adds d's padding.
+struct Layout {
+    uint32_t wtype = 0, scale_f16 = 0, rows = 0, cols = 0;
+    uint64_t q_bytes = 0, d_offset = 0, d_bytes = 0, min_span = 0, full_span = 0;
+};
+
+// QMV_OK or QMV_E_FORMAT / QMV_E_SHAPE; fills *L on success.
+int compute_layout(uint32_t wtype, uint32_t scale_f16, uint32_t rows,
+                   uint32_t cols, Layout* L);
+
+// Checks a host buffer holding the matrix's bytes: long enough, and no
+// Q8_0 quant equal to -128.  QMV_OK, QMV_E_ARG or QMV_E_FORMAT.
+int check_bytes(const Layout& L, const void* src, uint64_t nbytes);
+
+}  // namespace qmv

@@ -1,0 +1,195 @@
+"""Thin Python binding of libqmv (include/qmv.h): the same entry points, with
+arguments marshalled from PyTorch tensors (device memory) and streams.  All
+computation happens in the HIP library; if libqmv.so is missing, loading it
+raises instead of falling back to anything else."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmv.so")
+
+QMV_Q8_0 = 1
+QMV_Q4_0 = 2
+QMV_OK = 0
+QMV_E_ARG = -1
+QMV_E_FORMAT = -2
+QMV_E_SHAPE = -3
+QMV_E_DEVICE = -4
+QMV_E_NOMEM = -5
+
+# every symbol include/qmv.h declares
+EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
+           "qmv_destroy", "qmv_gemv", "qmv_gemm", "qmv_embed_rows",
+           "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str")
+
+_lib = None
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {qmv_status_str(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built: run `python -m block_quant_weight_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        u32, u64, i32, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
+        pu64 = ctypes.POINTER(u64)
+        sig = {
+            "qmv_span": ([u32, u32, u32, u32, pu64, pu64, pu64, pu64], i32),
+            "qmv_class_wtype": ([u32, u32, u32, u32, ctypes.POINTER(u32)], i32),
+            "qmv_create": ([ctypes.POINTER(vp), u32, u32, u32, u32], i32),
+            "qmv_upload": ([vp, vp, u64, vp], i32),
+            "qmv_destroy": ([vp], i32),
+            "qmv_gemv": ([vp, vp, vp, u32, vp], i32),
+            "qmv_gemm": ([vp, vp, vp, u32, vp], i32),
+            "qmv_embed_rows": ([vp, vp, u32, vp, vp], i32),
+            "qmv_quantize_q8": ([vp, u64, vp, vp, vp], i32),
+            "qmv_block_dots": ([vp, vp, vp, vp], i32),
+            "qmv_status_str": ([i32], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def qmv_status_str(status: int) -> str:
+    return lib().qmv_status_str(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != QMV_OK:
+        raise QmvError(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t, dtype, numel, what):
+    """Device pointer of a contiguous GPU tensor of at least `numel` elements."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{what} holds {t.numel()} elements, needs {numel}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class QmvHandle:
+    """A matrix handle: the C pointer plus the shape it was created with."""
+
+    def __init__(self, ptr, wtype, scale_f16, rows, cols):
+        self.ptr = ptr
+        self.wtype, self.scale_f16, self.rows, self.cols = wtype, scale_f16, rows, cols
+
+    def __repr__(self):
+        kind = {1: "Q8_0", 2: "Q4_0"}.get(self.wtype, "?")
+        return f"QmvHandle({kind}, f16 scales={bool(self.scale_f16)}, {self.rows}x{self.cols})"
+
+
+def qmv_span(wtype, scale_f16, rows, cols):
+    """dict(q_bytes, d_offset, d_bytes, min_span); raises QmvError."""
+    out = [ctypes.c_uint64(0) for _ in range(4)]
+    _check(lib().qmv_span(wtype, scale_f16, rows, cols, *[ctypes.byref(o) for o in out]),
+           "qmv_span")
+    return dict(zip(("q_bytes", "d_offset", "d_bytes", "min_span"), (o.value for o in out)))
+
+
+def qmv_class_wtype(file_wtype, q8_mask, class_bit, shared_classifier=0) -> int:
+    out = ctypes.c_uint32(0)
+    _check(lib().qmv_class_wtype(file_wtype, q8_mask, class_bit, shared_classifier,
+                                 ctypes.byref(out)), "qmv_class_wtype")
+    return out.value
+
+
+def qmv_create(wtype, scale_f16, rows, cols) -> QmvHandle:
+    p = ctypes.c_void_p(None)
+    _check(lib().qmv_create(ctypes.byref(p), wtype, scale_f16, rows, cols), "qmv_create")
+    return QmvHandle(p, wtype, scale_f16, rows, cols)
+
+
+def qmv_upload(h: QmvHandle, src, nbytes=None, stream=None):
+    """src: a host buffer (bytes, bytearray, numpy array) holding the matrix's
+    bytes from its q array on."""
+    import numpy as np
+    a = np.ascontiguousarray(np.frombuffer(src, dtype=np.uint8)
+                             if isinstance(src, (bytes, bytearray, memoryview))
+                             else np.asarray(src).view(np.uint8).reshape(-1))
+    n = a.size if nbytes is None else int(nbytes)
+    if n > a.size:
+        raise ValueError("nbytes exceeds the buffer")
+    st = lib().qmv_upload(h.ptr, a.ctypes.data_as(ctypes.c_void_p), n, _stream(stream))
+    _check(st, "qmv_upload")
+
+
+def qmv_destroy(h: QmvHandle):
+    if h is not None and h.ptr:
+        lib().qmv_destroy(h.ptr)
+        h.ptr = ctypes.c_void_p(None)
+
+
+def qmv_gemv(h: QmvHandle, x, y, batch=None, stream=None):
+    """x: float32 [batch, cols] on the GPU; y: float32 [batch, rows]."""
+    import torch
+    b = x.shape[0] if (batch is None and x.dim() == 2) else (batch or 1)
+    px = _dev(x, torch.float32, b * h.cols, "x")
+    py = _dev(y, torch.float32, b * h.rows, "y")
+    _check(lib().qmv_gemv(h.ptr, px, py, b, _stream(stream)), "qmv_gemv")
+
+
+def qmv_gemm(h: QmvHandle, x_bf16, y, batch=None, stream=None):
+    """x_bf16: bfloat16 (or int16/uint16 bit patterns) [batch, cols] on the
+    GPU; y: float32 [batch, rows]."""
+    import torch
+    b = x_bf16.shape[0] if batch is None else batch
+    if x_bf16.dtype in (torch.int16, torch.uint16):
+        x_bf16 = x_bf16.view(torch.bfloat16)
+    px = _dev(x_bf16, torch.bfloat16, b * h.cols, "x_bf16")
+    py = _dev(y, torch.float32, b * h.rows, "y")
+    _check(lib().qmv_gemm(h.ptr, px, py, b, _stream(stream)), "qmv_gemm")
+
+
+def qmv_embed_rows(h: QmvHandle, ids, out, stream=None):
+    """ids: int32 [n] on the GPU; out: float32 [n, cols]."""
+    import torch
+    n = ids.numel()
+    pi = _dev(ids, torch.int32, n, "ids")
+    po = _dev(out, torch.float32, n * h.cols, "out")
+    _check(lib().qmv_embed_rows(h.ptr, pi, n, po, _stream(stream)), "qmv_embed_rows")
+
+
+def qmv_quantize_q8(x, q, d, stream=None):
+    """x: float32 [n]; q: int8 [n]; d: float32 [n/32]; all on the GPU."""
+    import torch
+    n = x.numel()
+    px = _dev(x, torch.float32, n, "x")
+    pq = _dev(q, torch.int8, n, "q")
+    pd = _dev(d, torch.float32, n // 32, "d")
+    _check(lib().qmv_quantize_q8(px, n, pq, pd, _stream(stream)), "qmv_quantize_q8")
+
+
+def qmv_block_dots(h: QmvHandle, xq, s, stream=None):
+    """xq: int8 [cols]; s: int32 [rows, cols/32]; on the GPU."""
+    import torch
+    px = _dev(xq, torch.int8, h.cols, "xq")
+    ps = _dev(s, torch.int32, h.rows * (h.cols // 32), "s")
+    _check(lib().qmv_block_dots(h.ptr, px, ps, _stream(stream)), "qmv_block_dots")

@@ -1,0 +1,183 @@
+/*
+ * qmv.h - block-quantized weight matrix x activation products on one
+ * MI355X (gfx950) GPU.  Plain C ABI: no HIP, PyTorch or C++ types.
+ *
+ * A matrix is stored the way Krafla's ".mlb model, version 1" format page
+ * describes a quantized matrix ("Body", and the sections "Q8_0" and "Q4_0"):
+ *   - rows are outputs: y[r] = sum_c W[r][c] * x[c];
+ *   - two arrays, one after the other: q, the quants (Q8_0: rows*cols int8
+ *     bytes; Q4_0: rows*cols/2 bytes), then d, one scale per block of 32
+ *     consecutive weights of a row (f32, or IEEE f16 when scale_f16 = 1);
+ *   - each array is zero-padded to a multiple of 64 bytes, so d starts at
+ *     pad64(q bytes); the padding after d is optional;
+ *   - Q8_0: w = q * d, and a quant byte of -128 is not allowed;
+ *   - Q4_0: byte j of a block holds element j in its low nibble and element
+ *     j + 16 in its high nibble; w = (nibble - 8) * d;
+ *   - everything little-endian.
+ * Conventions this library fixes where the page is silent: row r's blocks
+ * (and scales) are consecutive, block k = r * (cols / 32) + c / 32; a
+ * dequantized weight is the single float32 product fl32(v * d) with IEEE
+ * signed zeros and subnormals; rows and cols are each at most 2^24 (the one
+ * limit the page's limits sentence keeps) and cols is a multiple of 32.
+ *
+ * Status: every function returns QMV_OK (0) or a negative QMV_E_* code.
+ * Errors are detected on the host before anything is launched; the classes
+ * follow the page's "Validation done by the loader" table (ML_E_FORMAT,
+ * ML_E_SHAPE), plus argument, device and memory errors.
+ *
+ * Streams: `stream` is a hipStream_t passed as a pointer; NULL is the null
+ * stream.  Compute calls only enqueue work on it and return; they never
+ * allocate device memory and never synchronize.
+ *
+ * Pointers: `x`, `y`, `ids`, `out`, `q`, `d`, `s` of the compute calls are
+ * device pointers owned by the caller, each 16-byte aligned (QMV_E_ARG
+ * otherwise).  The caller keeps them alive until the work on `stream` is
+ * done and must not let an output overlap an input.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct qmv_mat *qmv_handle;
+
+/* Storage types: the values of the .mlb header field "wtype". */
+enum { QMV_Q8_0 = 1, QMV_Q4_0 = 2 };
+
+enum {
+    QMV_OK = 0,
+    QMV_E_ARG = -1,    /* null pointer, misaligned pointer, zero batch/count,
+                          upload twice, compute before upload, wrong device */
+    QMV_E_FORMAT = -2, /* unknown wtype, scale_f16 not 0/1, buffer shorter
+                          than the arrays, a Q8_0 quant equal to -128 */
+    QMV_E_SHAPE = -3,  /* zero dimension, cols not a multiple of 32, a
+                          dimension above 2^24, size overflow */
+    QMV_E_DEVICE = -4, /* a HIP runtime error (launch or copy) */
+    QMV_E_NOMEM = -5   /* device or host allocation failed */
+};
+
+/*
+ * Sizes of a matrix's arrays, from the page's quantized-matrix paragraph:
+ * q_bytes = rows*cols (Q8_0) or rows*cols/2 (Q4_0); d_offset =
+ * pad64(q_bytes); d_bytes = rows*cols/32 * (scale_f16 ? 2 : 4); min_span =
+ * d_offset + d_bytes (the smallest buffer qmv_upload accepts).  Pure host
+ * arithmetic in uint64_t with overflow checks ("All size arithmetic is
+ * overflow-checked").  Any output pointer may be NULL.
+ * Errors: QMV_E_FORMAT (wtype, scale_f16), QMV_E_SHAPE (dimensions).
+ */
+int qmv_span(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
+             uint64_t *q_bytes, uint64_t *d_offset, uint64_t *d_bytes,
+             uint64_t *min_span);
+
+/*
+ * Storage type of one matrix class, from the page's q8_mask paragraph.
+ * class_bit is one of 1 tok_emb, 2 wcls, 4 wq/wk (wg, lqkv), 8 wv (lz),
+ * 16 wo (lout), 32 w1/w3, 64 w2.  A Q8_0 file (file_wtype 1) stores all
+ * classes as Q8_0.  In a Q4_0 file a set bit of q8_mask stores that class
+ * as Q8_0; with shared_classifier != 0 the embedding (also the classifier)
+ * is Q8_0 if bit 1 or bit 2 is set, and asking for class 2 names that same
+ * matrix.  Pure host arithmetic.
+ * Errors: QMV_E_FORMAT (file_wtype), QMV_E_ARG (class_bit not one of the
+ * seven bits, wtype_out NULL).
+ */
+int qmv_class_wtype(uint32_t file_wtype, uint32_t q8_mask, uint32_t class_bit,
+                    uint32_t shared_classifier, uint32_t *wtype_out);
+
+/*
+ * Creates an empty matrix handle of the given storage type and shape (no
+ * device memory yet).  *out receives the handle, owned by the caller until
+ * qmv_destroy.  Errors: QMV_E_ARG (out NULL), QMV_E_FORMAT, QMV_E_SHAPE
+ * (as qmv_span), QMV_E_NOMEM.
+ */
+int qmv_create(qmv_handle *out, uint32_t wtype, uint32_t scale_f16,
+               uint32_t rows, uint32_t cols);
+
+/*
+ * Copies one matrix's bytes, exactly as the file holds them starting at its
+ * q array (q, zero padding, d, optional trailing padding), from host memory
+ * `src` into one device allocation on the current device, keeping the
+ * file's offsets (d at d_offset) and the scales in their stored type.  The
+ * bytes are checked first: nbytes < min_span or a Q8_0 quant byte equal to
+ * 0x80 is QMV_E_FORMAT (padding bytes are not inspected).  Only the first
+ * min_span bytes are read.  The call waits for the copy on `stream`, so src
+ * may be released when it returns.  A handle is uploaded once and is then
+ * read-only; compute calls on several streams may share it.
+ * Errors: QMV_E_ARG (null, second upload), QMV_E_FORMAT, QMV_E_NOMEM,
+ * QMV_E_DEVICE.
+ */
+int qmv_upload(qmv_handle h, const void *src, uint64_t nbytes, void *stream);
+
+/* Releases the handle and its device memory.  The caller makes sure no work
+ * that reads it is still pending.  NULL is accepted.  Returns QMV_OK. */
+int qmv_destroy(qmv_handle h);
+
+/*
+ * Decode product (GEMV), y[t][r] = sum_c W[r][c] * x[t][c], for t < batch.
+ * x: float32 [batch][cols], y: float32 [batch][rows], row-major, device
+ * memory.  The weights stay quantized in device memory and are decoded in
+ * registers; accumulation is float32.  Each output is within
+ * 2e-3 * sum_c |W[r][c]| |x[t][c]| of the exact product.  Small batches run
+ * a bandwidth-bound vector kernel; large batches (an LM head over a prefill
+ * batch, say) run the matrix-core kernel with each float32 activation split
+ * into two bfloat16 terms.
+ * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no upload),
+ * QMV_E_DEVICE (launch failure).
+ */
+int qmv_gemv(qmv_handle h, const float *x, float *y, uint32_t batch,
+             void *stream);
+
+/*
+ * Prefill product (GEMM), y[t][r] = sum_c W[r][c] * x[t][c], with x given
+ * as bfloat16 bit patterns: x_bf16 uint16 [batch][cols], y float32
+ * [batch][rows], device memory.  Tiles of W are decoded to bfloat16
+ * (w rounded to nearest even) in LDS and multiplied on the matrix cores with
+ * float32 accumulation.  Errors: as qmv_gemv.
+ */
+int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
+             void *stream);
+
+/*
+ * Embedding-row gather: out[i][c] = fl32(v * d) of row ids[i], bit for bit
+ * the dequantized weight (scaling such as an embedding factor is the
+ * caller's).  ids: int32 [n], out: float32 [n][cols], device memory.  An id
+ * outside [0, rows) yields a row of zeros (memory stays safe; the host does
+ * not read ids).  Errors: QMV_E_ARG (null or misaligned pointer, n 0, no
+ * upload), QMV_E_DEVICE.
+ */
+int qmv_embed_rows(qmv_handle h, const int32_t *ids, uint32_t n, float *out,
+                   void *stream);
+
+/*
+ * Activation quantizer of the page's "Quantization rule", per block of 32
+ * consecutive values, in separate float32 operations (no fused
+ * multiply-add, correctly rounded divisions): amax = max |x|; amax < 1e-30
+ * gives d = 0 and q = 0; else d = amax / 127 and q = trunc(x * (127 / amax)
+ * + copysign(0.5, x)) clamped to [-127, 127].  x: float32 [n], q: int8 [n],
+ * d: float32 [n / 32], device memory; n a multiple of 32.
+ * Errors: QMV_E_ARG (null or misaligned pointer, n 0), QMV_E_SHAPE
+ * (n % 32 != 0), QMV_E_DEVICE.
+ */
+int qmv_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d,
+                    void *stream);
+
+/*
+ * Per-block integer dot products of the weight quants with quantized
+ * activations: s[r][b] = sum_{j<32} v[r][32b + j] * xq[32b + j] in int32,
+ * exact (v the Q8_0 quant or Q4_0 nibble - 8).  xq: int8 [cols],
+ * s: int32 [rows][cols / 32], device memory.
+ * Errors: QMV_E_ARG (null or misaligned pointer, no upload), QMV_E_DEVICE.
+ */
+int qmv_block_dots(qmv_handle h, const int8_t *xq, int32_t *s, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *qmv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

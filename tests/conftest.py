@@ -14,3 +14,13 @@ if HERE not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _name_gpu_case(request):
+    # Before a GPU test runs, name it on the real stderr (not captured) and
+    # flush, so that a run that ends the process still shows the case.
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
