@@ -25,17 +25,44 @@ __device__ __forceinline__ float load_scale(const void* __restrict__ d, uint64_t
     }
 }
 
+// Raw bits of scale k (f16 in the low half, or f32), and their value.
+template <bool SF16>
+__device__ __forceinline__ uint32_t load_scale_bits(const void* __restrict__ d, uint64_t k) {
+    if constexpr (SF16) return static_cast<const uint16_t*>(d)[k];
+    else return static_cast<const uint32_t*>(d)[k];
+}
+template <bool SF16>
+__device__ __forceinline__ float scale_from_bits(uint32_t b) {
+    if constexpr (SF16)
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+    else return __builtin_bit_cast(float, b);
+}
+
 // Byte i (0..3) of a 32-bit word converted to float (v_cvt_f32_ubyteN).
 template <int I>
 __device__ __forceinline__ float ubyte_f32(uint32_t w) {
     return static_cast<float>((w >> (8 * I)) & 0xFFu);
 }
 
-// Sum over the 64 lanes of a wavefront; every lane gets the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wavefront, returned in every lane.  DPP moves
+// reduce each row of 16 lanes (swap neighbours, swap pairs, rotate by 4 and
+// by 8), then the four row sums are read out and added in a fixed order.
+__device__ __forceinline__ float wave_reduce(float v) {
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 }  // namespace qmv
