@@ -206,7 +206,10 @@ def main():
 
     desc, kind, config, mats, batch = workload(args.workload)
     torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
+    # One side stream for warm-up, capture and timing: the library keeps its
+    # split-K workspace per stream, so the capture stream must be warmed up.
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
 
     if kind == "copy":
         n = 256 << 20
@@ -281,7 +284,7 @@ def main():
     use_graph = not args.no_graph
     if use_graph:
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=stream):
             for i in range(steps):
                 step(warmup + i)
         g.replay()                        # untimed: first replay uploads the graph

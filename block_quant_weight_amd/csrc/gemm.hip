@@ -206,6 +206,300 @@ __global__ __launch_bounds__(256) void gemm_kernel(
             }
 }
 
+// ---------------------------------------------------------------------------
+// Large-batch kernel: tile 256 tokens x 128 matrix rows, BK = 64.
+//
+// Four waves (2 x 2), each multiplying 128 tokens x 64 rows (4 x 2 tiles of
+// 32x32) per 16-wide k slice: 6 LDS fragment reads feed 8 MFMAs, which keeps
+// the LDS traffic of the four waves at 96 bytes per clock of a compute unit.
+// The weights of a tile are decoded once per workgroup and shared by all
+// 256 tokens (one quant block per thread per step).  Decoding uses
+// fma(v_u, d, -OFF*d) = fl32((v_u - OFF) * d), bit-identical to the single
+// f32 product v * d, then v_cvt_pk_bf16_f32 (round to nearest even).
+//
+// Pipeline: LDS is double-buffered; global loads for step s + 2 are issued
+// into a register set before step s is multiplied, and the set of step s + 1
+// is written to the other LDS buffer after it (two register sets suffice).
+// All loads are raw buffer loads; rows, tokens and k past the end get an
+// out-of-range offset (zeros, no traffic), so the loop has no branch around
+// a load.  With split-K (grid.z) each slice writes its partial tile to a
+// workspace that a second kernel sums in slice order.
+// ---------------------------------------------------------------------------
+
+namespace big {
+
+constexpr int BM = 256, BN = 128, BK = 64, LDK = BK + 8;
+constexpr int XSEG = BM * BK / 8 / 256;  // 16-byte activation segments per thread per step
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOob = 0xFFFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : static_cast<uint32_t>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(n), 0x00020000);
+}
+
+template <uint32_t WT>
+struct Stage {                 // one step's global data, held in registers
+    uint4 xs[XSEG];            // bf16 activations, 8 per segment
+    uint4 q[WT == kQ4 ? 1 : 2];  // one quant block
+    uint32_t d;                // its scale bits
+};
+
+template <uint32_t WT, bool SF16>
+struct Ctx {
+    __amdgpu_buffer_rsrc_t xr, qr, dr;
+    uint32_t M, N, K, m0, n0, ke;
+    int tid;
+    // fetch step k0 into st (k0 may be past ke: then everything is out of range)
+    __device__ __forceinline__ void fetch(uint32_t k0, Stage<WT>& st) const {
+#pragma unroll
+        for (int i = 0; i < XSEG; ++i) {
+            const int seg = tid + 256 * i;
+            const uint32_t r = seg >> 3, c8 = (seg & 7) * 8;
+            const uint32_t m = m0 + r, k = k0 + c8;
+            const uint32_t off = (m < M && k < ke) ? (m * K + k) * 2 : kOob;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+            st.xs[i] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+        const uint32_t r = tid >> 1, b = tid & 1;
+        const uint32_t n = n0 + r, k = k0 + 32 * b;
+        const bool ok = n < N && k < ke;
+        const uint32_t blk = n * (K >> 5) + (k >> 5);
+        constexpr uint32_t QB = (WT == kQ4) ? 16 : 32;
+#pragma unroll
+        for (int j = 0; j < QB / 16; ++j) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qr, ok ? blk * QB + 16 * j : kOob, 0, 0);
+            st.q[j] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+        if constexpr (SF16) st.d = __builtin_amdgcn_raw_buffer_load_b16(dr, ok ? blk * 2 : kOob, 0, 0);
+        else st.d = __builtin_amdgcn_raw_buffer_load_b32(dr, ok ? blk * 4 : kOob, 0, 0);
+    }
+};
+
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = static_cast<__bf16>(a);
+    v[1] = static_cast<__bf16>(b);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Write step data to LDS in four parts (one per 16-wide k slice of the MFMA
+// loop, so that the decode work interleaves with the matrix cores): parts 0
+// and 1 copy the activations, parts 2 and 3 decode half of the quant block
+// each (elements 0..7 + 16..23, then 8..15 + 24..31) to bf16.
+template <uint32_t WT, bool SF16, int PART>
+__device__ __forceinline__ void store_part(const Stage<WT>& st, __bf16* __restrict__ xs,
+                                           __bf16* __restrict__ ws, int tid) {
+    if constexpr (PART < 2) {
+#pragma unroll
+        for (int i = PART * XSEG / 2; i < (PART + 1) * XSEG / 2; ++i) {
+            const int seg = tid + 256 * i;
+            const int r = seg >> 3, c8 = (seg & 7) * 8;
+            *reinterpret_cast<uint4*>(&xs[r * LDK + c8]) = st.xs[i];
+        }
+    } else {
+        constexpr int H = PART - 2;  // which half of the block
+        const float dv = scale_from_bits<SF16>(st.d);
+        uint32_t o0[4], o1[4];       // bf16 pairs of the two 8-element runs
+        if constexpr (WT == kQ4) {
+            // w = (n - 8) d = fma(n, d, -8d): n d and 8 d are exact, one rounding
+            const float m8d = -8.f * dv;
+            uint32_t mask = 0x0F0F0F0Fu;
+            asm("" : "+v"(mask));
+            const uint32_t w[2] = {H == 0 ? st.q[0].x : st.q[0].z, H == 0 ? st.q[0].y : st.q[0].w};
+            float lo[8], hi[8];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t l = w[i] & mask, h = (w[i] >> 4) & mask;
+                lo[4 * i + 0] = fmaf(ubyte_f32<0>(l), dv, m8d);
+                lo[4 * i + 1] = fmaf(ubyte_f32<1>(l), dv, m8d);
+                lo[4 * i + 2] = fmaf(ubyte_f32<2>(l), dv, m8d);
+                lo[4 * i + 3] = fmaf(ubyte_f32<3>(l), dv, m8d);
+                hi[4 * i + 0] = fmaf(ubyte_f32<0>(h), dv, m8d);
+                hi[4 * i + 1] = fmaf(ubyte_f32<1>(h), dv, m8d);
+                hi[4 * i + 2] = fmaf(ubyte_f32<2>(h), dv, m8d);
+                hi[4 * i + 3] = fmaf(ubyte_f32<3>(h), dv, m8d);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o0[i] = pk_bf16(lo[2 * i], lo[2 * i + 1]);   // elements 8H + 2i..
+                o1[i] = pk_bf16(hi[2 * i], hi[2 * i + 1]);   // elements 16 + 8H + 2i..
+            }
+        } else {
+            // w = q d = fma(q + 128, d, -128 d): one rounding of the exact q d
+            const float m128d = -128.f * dv;
+            const uint4 a = st.q[H];  // elements 16H .. 16H + 15
+            const uint32_t w[4] = {a.x ^ 0x80808080u, a.y ^ 0x80808080u, a.z ^ 0x80808080u,
+                                   a.w ^ 0x80808080u};
+            uint32_t o[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[2 * i] = pk_bf16(fmaf(ubyte_f32<0>(w[i]), dv, m128d), fmaf(ubyte_f32<1>(w[i]), dv, m128d));
+                o[2 * i + 1] = pk_bf16(fmaf(ubyte_f32<2>(w[i]), dv, m128d), fmaf(ubyte_f32<3>(w[i]), dv, m128d));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o0[i] = o[i];
+                o1[i] = o[4 + i];
+            }
+        }
+        const int r = tid >> 1, b = tid & 1;
+        __bf16* row = &ws[r * LDK + 32 * b];
+        if constexpr (WT == kQ4) {
+            *reinterpret_cast<uint4*>(row + 8 * H) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+            *reinterpret_cast<uint4*>(row + 16 + 8 * H) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        } else {
+            *reinterpret_cast<uint4*>(row + 16 * H) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+            *reinterpret_cast<uint4*>(row + 16 * H + 8) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+        }
+    }
+}
+
+template <uint32_t WT, bool SF16>
+__device__ __forceinline__ void store_stage(const Stage<WT>& st, __bf16* __restrict__ xs,
+                                            __bf16* __restrict__ ws, int tid) {
+    store_part<WT, SF16, 0>(st, xs, ws, tid);
+    store_part<WT, SF16, 1>(st, xs, ws, tid);
+    store_part<WT, SF16, 2>(st, xs, ws, tid);
+    store_part<WT, SF16, 3>(st, xs, ws, tid);
+}
+
+template <uint32_t WT, bool SF16>
+__global__ __launch_bounds__(256) void gemm_big_kernel(
+    const uint8_t* __restrict__ q, const void* __restrict__ d, const uint16_t* __restrict__ x,
+    float* __restrict__ y, float* __restrict__ ws_partial, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t k_per_split) {
+    constexpr int TM = 4, TN = 2;
+    __shared__ __attribute__((aligned(16))) __bf16 Xs[2][BM * LDK];
+    __shared__ __attribute__((aligned(16))) __bf16 Ws[2][BN * LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid >> 1, wn = wid & 1;
+    Ctx<WT, SF16> c;
+    c.M = M; c.N = N; c.K = K; c.tid = tid;
+    c.m0 = blockIdx.y * BM;
+    c.n0 = blockIdx.x * BN;
+    const uint32_t kb = blockIdx.z * k_per_split;
+    c.ke = min(K, kb + k_per_split);
+    c.xr = rsrc(x, static_cast<uint64_t>(M) * K * 2);
+    const uint64_t qbytes = (WT == kQ4) ? static_cast<uint64_t>(N) * K / 2 : static_cast<uint64_t>(N) * K;
+    c.qr = rsrc(q, qbytes);
+    c.dr = rsrc(d, static_cast<uint64_t>(N) * (K / 32) * (SF16 ? 2 : 4));
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    Stage<WT> sa, sb;
+    c.fetch(kb, sa);
+    c.fetch(kb + BK, sb);
+    store_stage<WT, SF16>(sa, Xs[0], Ws[0], tid);
+    __syncthreads();
+
+    // One step: the 4 k slices of MFMAs on LDS buffer `cur`, with the
+    // store of the next step's data (register set `nx`) into the other buffer
+    // split into four parts between them.
+    auto step = [&](int cur, const Stage<WT>& nx) {
+        const __bf16* __restrict__ xs = Xs[cur];
+        const __bf16* __restrict__ wsb = Ws[cur];
+        __bf16* __restrict__ xn = Xs[cur ^ 1];
+        __bf16* __restrict__ wn_ = Ws[cur ^ 1];
+        bf16x8 a[2][TM], b[2][TN];
+        auto frags = [&](int kk, int set) {
+            const int kc = kk + 8 * (lane >> 5);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                a[set][i] = *reinterpret_cast<const bf16x8*>(&xs[(wm * 128 + i * 32 + (lane & 31)) * LDK + kc]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b[set][j] = *reinterpret_cast<const bf16x8*>(&wsb[(wn * 64 + j * 32 + (lane & 31)) * LDK + kc]);
+        };
+        auto mm = [&](int set) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[set][i], b[set][j], acc[i][j], 0, 0, 0);
+        };
+        frags(0, 0);
+        frags(16, 1);
+        mm(0);
+        store_part<WT, SF16, 0>(nx, xn, wn_, tid);
+        frags(32, 0);
+        mm(1);
+        store_part<WT, SF16, 2>(nx, xn, wn_, tid);
+        frags(48, 1);
+        mm(0);
+        store_part<WT, SF16, 1>(nx, xn, wn_, tid);
+        mm(1);
+        store_part<WT, SF16, 3>(nx, xn, wn_, tid);
+    };
+
+    // Step s reads LDS[s & 1]; sa/sb alternate as the register set of step
+    // s + 1.  The loop exit sits after the barrier so that each step's MFMAs
+    // and the next step's stores form one block the scheduler can
+    // interleave; the last step stores (zeros) into the unused buffer.
+    uint32_t k0 = kb;
+    for (;;) {
+        c.fetch(k0 + 2 * BK, sa);          // step s + 2
+        step(0, sb);
+        __syncthreads();
+        if (k0 + BK >= c.ke) break;
+        c.fetch(k0 + 3 * BK, sb);
+        step(1, sa);
+        __syncthreads();
+        k0 += 2 * BK;
+        if (k0 >= c.ke) break;
+    }
+
+    // epilogue: lane holds column n = lane % 32, rows 8 (v / 4) + 4 (lane / 32) + v % 4
+    float* out = ws_partial ? ws_partial + static_cast<uint64_t>(blockIdx.z) * M * N : y;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t m = c.m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const uint32_t n = c.n0 + wn * 64 + j * 32 + (lane & 31);
+                if (m < M && n < N) out[static_cast<uint64_t>(m) * N + n] = acc[i][j][v];
+            }
+}
+
+// y = sum of the split-K partials, in slice order (deterministic).  Slice z
+// starts at part + z * total; with total % 4 == 0 every slice is 16-byte
+// aligned and each thread adds float4s, else single floats.
+template <bool VEC>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            float* __restrict__ y, uint64_t total,
+                                                            uint32_t splits) {
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if constexpr (VEC) {
+        if (4 * i >= total) return;
+        const float4* p = reinterpret_cast<const float4*>(part);
+        const uint64_t t4 = total / 4;
+        float4 s = p[i];
+        for (uint32_t z = 1; z < splits; ++z) {
+            const float4 t = p[z * t4 + i];
+            s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+        }
+        reinterpret_cast<float4*>(y)[i] = s;
+    } else {
+        if (i >= total) return;
+        float s = part[i];
+        for (uint32_t z = 1; z < splits; ++z) s += part[z * total + i];
+        y[i] = s;
+    }
+}
+
+}  // namespace big
+
 template <uint32_t WT, bool SF16, bool XF32>
 hipError_t gemm_dispatch(const MatView& m, const void* x, float* y,
                          uint32_t batch, hipStream_t s) {
@@ -234,8 +528,83 @@ hipError_t gemm_by_type(const MatView& m, const void* x, float* y,
 
 }  // namespace
 
+namespace {
+
+// Shape of the large-batch launch: tiles and split-K slices.
+struct BigPlan {
+    bool use = false;
+    uint32_t tiles_n = 0, tiles_m = 0, splits = 1, k_per_split = 0;
+};
+
+BigPlan big_plan(const MatView& m, uint32_t batch, bool x_f32) {
+    BigPlan p;
+    if (x_f32 || batch < 128) return p;
+    // 32-bit buffer offsets over the activations, quants and scales
+    const uint64_t qbytes = (m.wtype == kQ4) ? uint64_t{m.rows} * m.cols / 2
+                                             : uint64_t{m.rows} * m.cols;
+    if (uint64_t{batch} * m.cols * 2 >= 0xFFFFFFF0ull || qbytes >= 0xFFFFFFF0ull ||
+        uint64_t{m.rows} * (m.cols / 32) * 4 >= 0xFFFFFFF0ull)
+        return p;
+    p.use = true;
+    p.tiles_n = (m.rows + big::BN - 1) / big::BN;
+    p.tiles_m = (batch + big::BM - 1) / big::BM;
+    const uint32_t tiles = p.tiles_n * p.tiles_m;
+    const uint32_t steps = (m.cols + big::BK - 1) / big::BK;
+    // too few tiles for 256 compute units: split K, keeping >= 8 steps a slice
+    uint32_t splits = 1;
+    while (tiles * splits * 2 <= 320 && steps / (splits * 2) >= 8) splits *= 2;
+    const uint32_t per = (steps + splits - 1) / splits;
+    p.k_per_split = per * big::BK;
+    p.splits = (m.cols + p.k_per_split - 1) / p.k_per_split;
+    return p;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32) {
+    const BigPlan p = big_plan(m, batch, x_f32);
+    if (!p.use || p.splits == 1) return 0;
+    return static_cast<size_t>(p.splits) * batch * m.rows * sizeof(float);
+}
+
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
-                       uint32_t batch, hipStream_t s) {
+                       uint32_t batch, float* workspace, hipStream_t s) {
+    const BigPlan p = big_plan(m, batch, x_f32);
+    if (p.use) {
+        if (p.tiles_m > 65535u || p.splits > 65535u) return hipErrorInvalidValue;
+        float* part = p.splits > 1 ? workspace : nullptr;
+        if (p.splits > 1 && part == nullptr) return hipErrorInvalidValue;
+        const dim3 grid(p.tiles_n, p.tiles_m, p.splits);
+        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        if (m.wtype == kQ4) {
+            if (m.scale_f16)
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, true>), grid, dim3(256), 0, s,
+                                   m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
+            else
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, false>), grid, dim3(256), 0, s,
+                                   m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
+        } else {
+            if (m.scale_f16)
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, true>), grid, dim3(256), 0, s,
+                                   m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
+            else
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, false>), grid, dim3(256), 0, s,
+                                   m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.splits == 1) return e;
+        const uint64_t total = static_cast<uint64_t>(batch) * m.rows;
+        const bool vec = total % 4 == 0;
+        const uint64_t blocks = ((vec ? total / 4 : total) + 255) / 256;
+        if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+        if (vec)
+            hipLaunchKernelGGL(big::splitk_reduce_kernel<true>, dim3(static_cast<uint32_t>(blocks)),
+                               dim3(256), 0, s, part, y, total, p.splits);
+        else
+            hipLaunchKernelGGL(big::splitk_reduce_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
+                               dim3(256), 0, s, part, y, total, p.splits);
+        return hipGetLastError();
+    }
     // grid.y carries the token tiles: at most 65535 of them
     if ((batch + 63) / 64 > 65535u) return hipErrorInvalidValue;
     return x_f32 ? gemm_by_type<true>(m, x, y, batch, s)

@@ -518,7 +518,7 @@ constexpr uint32_t kGemvMaxBatch = 8;
 
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
                        uint32_t batch, hipStream_t s) {
-    if (batch > kGemvMaxBatch) return launch_gemm(m, x, true, y, batch, s);
+    if (batch > kGemvMaxBatch) return launch_gemm(m, x, true, y, batch, nullptr, s);
     if (m.wtype == kQ4) {
         return m.scale_f16 ? gemv_batched<kQ4, true>(m, x, y, batch, s)
                            : gemv_batched<kQ4, false>(m, x, y, batch, s);

@@ -18,9 +18,12 @@ hipError_t launch_gemv(const MatView& m, const float* x, float* y,
                        uint32_t batch, hipStream_t stream);
 
 // Same product on the matrix cores: x is bf16 bits, or f32 split into two
-// bf16 terms (x_f32 = true).
+// bf16 terms (x_f32 = true).  Large batches may split K; the slices' partial
+// sums then go to `workspace` (gemm_workspace_bytes of them; ignored when
+// that is 0).
+size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
-                       uint32_t batch, hipStream_t stream);
+                       uint32_t batch, float* workspace, hipStream_t stream);
 
 // out[i][c] = fl32(v * d) of row ids[i] (zeros for an id out of range).
 hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,

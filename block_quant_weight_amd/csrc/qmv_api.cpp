@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "kernels.h"
 #include "qmv.h"
@@ -35,6 +37,51 @@ int ready(const qmv_mat* h) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return QMV_E_DEVICE;
     if (cur != h->device) return QMV_E_ARG;
+    return QMV_OK;
+}
+
+// Split-K workspace, one per (device, stream): work on one stream runs in
+// order, so every call on that stream may reuse it; calls on other streams
+// get their own.  It grows on demand.  A replaced buffer is never freed (a
+// graph captured earlier may still name it); all live until the process
+// ends.
+struct Workspace {
+    int device;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+int workspace_for(hipStream_t stream, size_t bytes, void** out) {
+    *out = nullptr;
+    if (bytes == 0) return QMV_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace* w = nullptr;
+    for (auto& e : g_ws)
+        if (e.device == dev && e.stream == stream) w = &e;
+    if (w != nullptr && w->bytes >= bytes) {
+        *out = w->ptr;
+        return QMV_OK;
+    }
+    // Growing allocates: not allowed while the stream is being captured into
+    // a graph (run the call once on that stream before capturing it).
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return QMV_E_DEVICE;
+    if (cap != hipStreamCaptureStatusNone) return QMV_E_ARG;
+    void* p = nullptr;
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? QMV_E_NOMEM : QMV_E_DEVICE;
+    if (w != nullptr) {
+        w->ptr = p;  // the old buffer stays allocated (see above)
+        w->bytes = bytes;
+    } else {
+        g_ws.push_back(Workspace{dev, stream, p, bytes});
+    }
+    *out = p;
     return QMV_OK;
 }
 
@@ -119,8 +166,13 @@ int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
     if (st != QMV_OK) return st;
     if (x_bf16 == nullptr || y == nullptr || batch == 0) return QMV_E_ARG;
     if (!aligned16(x_bf16) || !aligned16(y)) return QMV_E_ARG;
-    return device_status(qmv::launch_gemm(view(h), x_bf16, false, y, batch,
-                                          static_cast<hipStream_t>(stream)));
+    const qmv::MatView v = view(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = workspace_for(s, qmv::gemm_workspace_bytes(v, batch, false), &ws);
+    if (st != QMV_OK) return st;
+    return device_status(qmv::launch_gemm(v, x_bf16, false, y, batch,
+                                          static_cast<float*>(ws), s));
 }
 
 int qmv_embed_rows(qmv_handle h, const int32_t* ids, uint32_t n, float* out,

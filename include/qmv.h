@@ -27,7 +27,11 @@
  *
  * Streams: `stream` is a hipStream_t passed as a pointer; NULL is the null
  * stream.  Compute calls only enqueue work on it and return; they never
- * allocate device memory and never synchronize.
+ * synchronize.  The one exception to "no allocation": a large-batch
+ * qmv_gemm that splits K keeps its partial sums in a workspace owned by the
+ * library, one per (device, stream), allocated on first need and grown (never
+ * freed) for a larger batch; that first call on a stream must not be made
+ * while the stream is being captured into a graph (QMV_E_ARG).
  *
  * Pointers: `x`, `y`, `ids`, `out`, `q`, `d`, `s` of the compute calls are
  * device pointers owned by the caller, each 16-byte aligned (QMV_E_ARG
@@ -135,7 +139,11 @@ int qmv_gemv(qmv_handle h, const float *x, float *y, uint32_t batch,
  * as bfloat16 bit patterns: x_bf16 uint16 [batch][cols], y float32
  * [batch][rows], device memory.  Tiles of W are decoded to bfloat16
  * (w rounded to nearest even) in LDS and multiplied on the matrix cores with
- * float32 accumulation.  Errors: as qmv_gemv.
+ * float32 accumulation.  When the matrix has too few tiles to fill the GPU
+ * the K dimension is split and the slices' partial sums are added in slice
+ * order by a second kernel (deterministic).  Errors: as qmv_gemv, plus
+ * QMV_E_ARG for a first split-K call on a stream under graph capture and
+ * QMV_E_NOMEM if its workspace cannot be allocated.
  */
 int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
              void *stream);

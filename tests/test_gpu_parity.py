@@ -166,7 +166,8 @@ def test_gemv_is_deterministic():
 
 @pytest.mark.parametrize("wt,sf", [(1, 0), (1, 1), (2, 0), (2, 1)])
 @pytest.mark.parametrize("R,C,B", [(1, 32, 1), (129, 96, 33), (200, 4160, 130),
-                                   (128, 64, 64), (257, 1024, 7)])
+                                   (128, 64, 64), (257, 1024, 7), (300, 96, 256),
+                                   (130, 1056, 200), (1, 2048, 513)])
 def test_gemm_small_full(wt, sf, R, C, B):
     img = K.make_image(400 + B, R, wt, sf, R, C, lo=-1e-2)
     h = K.upload(img, wt, sf, R, C)
@@ -262,5 +263,22 @@ def test_gpu_argument_errors():
         assert L.qmv_gemv(h.ptr, bad, ctypes.c_void_p(y.data_ptr()), 1, None) == Q.QMV_E_ARG
         assert L.qmv_gemv(h.ptr, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
                           0, None) == Q.QMV_E_ARG
+    finally:
+        Q.qmv_destroy(h)
+
+
+def test_gemm_split_k_is_deterministic():
+    # a narrow matrix with a long K takes the split-K path; partial sums are
+    # added in slice order, so two runs agree bit for bit
+    R, C, B = 256, 8192, 256
+    img = K.make_image(450, 0, 1, 0, R, C)
+    h = K.upload(img, 1, 0, R, C)
+    try:
+        xb = K.make_xb(450, 1, B, C)
+        a, b = K.gpu_gemm(h, xb), K.gpu_gemm(h, xb)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        sel = np.array([0, 1, 127, 128, 255])
+        ref, norm = O.product(img, 1, 0, R, C, xb, sel=sel, threads=K.THREADS)
+        close(a[:, sel], ref, norm, "split-K gemm")
     finally:
         Q.qmv_destroy(h)
