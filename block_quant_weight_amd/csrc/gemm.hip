@@ -209,29 +209,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 // ---------------------------------------------------------------------------
 // Large-batch kernel: tile 256 tokens x 128 matrix rows, BK = 64.
 //
-// Four waves (2 x 2), each multiplying 128 tokens x 64 rows (4 x 2 tiles of
-// 32x32) per 16-wide k slice: 6 LDS fragment reads feed 8 MFMAs, which keeps
-// the LDS traffic of the four waves at 96 bytes per clock of a compute unit.
-// The weights of a tile are decoded once per workgroup and shared by all
-// 256 tokens (one quant block per thread per step).  Decoding uses
-// fma(v_u, d, -OFF*d) = fl32((v_u - OFF) * d), bit-identical to the single
-// f32 product v * d, then v_cvt_pk_bf16_f32 (round to nearest even).
+// Eight waves in two groups of four.  Within a group the waves are 2 x 2,
+// each multiplying 128 tokens x 64 rows (4 x 2 tiles of 32x32) per 16-wide
+// k slice: 6 LDS fragment reads feed 8 MFMAs.  Group 0 takes k slices 0 and
+// 2 of every step, group 1 slices 1 and 3, so each SIMD runs two waves (one
+// stalls, the other issues) while the LDS traffic per MFMA stays that of a
+// 128 x 64 wave tile; the groups' sums are added through LDS at the end.
+// The weights of a tile are decoded once per workgroup: each thread decodes
+// half a quant block per step with fma(code, d, -OFF*d) = fl32((code - OFF)
+// * d), bit-identical to the single f32 product v * d, then
+// v_cvt_pk_bf16_f32 (round to nearest even).
 //
 // Pipeline: LDS is double-buffered; global loads for step s + 2 are issued
 // into a register set before step s is multiplied, and the set of step s + 1
-// is written to the other LDS buffer after it (two register sets suffice).
-// All loads are raw buffer loads; rows, tokens and k past the end get an
-// out-of-range offset (zeros, no traffic), so the loop has no branch around
-// a load.  With split-K (grid.z) each slice writes its partial tile to a
-// workspace that a second kernel sums in slice order.
+// is written to the other LDS buffer in parts between the k slices.  All
+// loads are raw buffer loads; rows, tokens and k past the end get an
+// out-of-range offset (zeros, no traffic).  With split-K (grid.z) each slice
+// writes its partial tile to a workspace that a second kernel sums in slice
+// order.
 // ---------------------------------------------------------------------------
 
 namespace big {
 
 constexpr int BM = 256, BN = 128, BK = 64, LDK = BK + 8;
-constexpr int XSEG = BM * BK / 8 / 256;  // 16-byte activation segments per thread per step
+constexpr int NT = 512;                   // threads per workgroup
+constexpr int XSEG = BM * BK / 8 / NT;    // 16-byte activation segments per thread per step
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr uint32_t kOob = 0xFFFFFFF0u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_t bytes) {
@@ -240,11 +245,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint64_
                                              static_cast<int>(n), 0x00020000);
 }
 
+// One step's global data held by a thread: XSEG activation segments and half
+// a quant block (Q4_0: 8 bytes, Q8_0: 16 bytes) with its scale.
 template <uint32_t WT>
-struct Stage {                 // one step's global data, held in registers
-    uint4 xs[XSEG];            // bf16 activations, 8 per segment
-    uint4 q[WT == kQ4 ? 1 : 2];  // one quant block
-    uint32_t d;                // its scale bits
+struct Stage {
+    uint4 xs[XSEG];
+    uint32_t q[WT == kQ4 ? 2 : 4];
+    uint32_t d;
 };
 
 template <uint32_t WT, bool SF16>
@@ -256,22 +263,28 @@ struct Ctx {
     __device__ __forceinline__ void fetch(uint32_t k0, Stage<WT>& st) const {
 #pragma unroll
         for (int i = 0; i < XSEG; ++i) {
-            const int seg = tid + 256 * i;
+            const int seg = tid + NT * i;
             const uint32_t r = seg >> 3, c8 = (seg & 7) * 8;
             const uint32_t m = m0 + r, k = k0 + c8;
             const uint32_t off = (m < M && k < ke) ? (m * K + k) * 2 : kOob;
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
             st.xs[i] = make_uint4(v[0], v[1], v[2], v[3]);
         }
-        const uint32_t r = tid >> 1, b = tid & 1;
+        // thread -> (row r, block b, half h) of the 128 x 2 blocks
+        const uint32_t r = tid >> 2, b = (tid >> 1) & 1, h = tid & 1;
         const uint32_t n = n0 + r, k = k0 + 32 * b;
         const bool ok = n < N && k < ke;
         const uint32_t blk = n * (K >> 5) + (k >> 5);
-        constexpr uint32_t QB = (WT == kQ4) ? 16 : 32;
-#pragma unroll
-        for (int j = 0; j < QB / 16; ++j) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qr, ok ? blk * QB + 16 * j : kOob, 0, 0);
-            st.q[j] = make_uint4(v[0], v[1], v[2], v[3]);
+        if constexpr (WT == kQ4) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(qr, ok ? blk * 16 + 8 * h : kOob, 0, 0);
+            st.q[0] = v[0];
+            st.q[1] = v[1];
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qr, ok ? blk * 32 + 16 * h : kOob, 0, 0);
+            st.q[0] = v[0];
+            st.q[1] = v[1];
+            st.q[2] = v[2];
+            st.q[3] = v[3];
         }
         if constexpr (SF16) st.d = __builtin_amdgcn_raw_buffer_load_b16(dr, ok ? blk * 2 : kOob, 0, 0);
         else st.d = __builtin_amdgcn_raw_buffer_load_b32(dr, ok ? blk * 4 : kOob, 0, 0);
@@ -286,89 +299,68 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Write step data to LDS in four parts (one per 16-wide k slice of the MFMA
-// loop, so that the decode work interleaves with the matrix cores): parts 0
-// and 1 copy the activations, parts 2 and 3 decode half of the quant block
-// each (elements 0..7 + 16..23, then 8..15 + 24..31) to bf16.
+// Write step data to LDS in two parts (placed between the k slices so the
+// decode interleaves with the matrix cores): part 0 copies the activation
+// segments, part 1 decodes the thread's half block to bf16.  Q4_0 half h
+// holds bytes 8h .. 8h + 7: elements 8h .. 8h + 7 (low nibbles) and
+// 16 + 8h .. 16 + 8h + 7 (high nibbles).  Q8_0 half h is elements 16h ..
+// 16h + 15.
 template <uint32_t WT, bool SF16, int PART>
 __device__ __forceinline__ void store_part(const Stage<WT>& st, __bf16* __restrict__ xs,
                                            __bf16* __restrict__ ws, int tid) {
-    if constexpr (PART < 2) {
+    if constexpr (PART == 0) {
 #pragma unroll
-        for (int i = PART * XSEG / 2; i < (PART + 1) * XSEG / 2; ++i) {
-            const int seg = tid + 256 * i;
+        for (int i = 0; i < XSEG; ++i) {
+            const int seg = tid + NT * i;
             const int r = seg >> 3, c8 = (seg & 7) * 8;
             *reinterpret_cast<uint4*>(&xs[r * LDK + c8]) = st.xs[i];
         }
     } else {
-        constexpr int H = PART - 2;  // which half of the block
         const float dv = scale_from_bits<SF16>(st.d);
-        uint32_t o0[4], o1[4];       // bf16 pairs of the two 8-element runs
+        const int r = tid >> 2, b = (tid >> 1) & 1, h = tid & 1;
+        __bf16* row = &ws[r * LDK + 32 * b];
         if constexpr (WT == kQ4) {
             // w = (n - 8) d = fma(n, d, -8d): n d and 8 d are exact, one rounding
             const float m8d = -8.f * dv;
             uint32_t mask = 0x0F0F0F0Fu;
             asm("" : "+v"(mask));
-            const uint32_t w[2] = {H == 0 ? st.q[0].x : st.q[0].z, H == 0 ? st.q[0].y : st.q[0].w};
             float lo[8], hi[8];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const uint32_t l = w[i] & mask, h = (w[i] >> 4) & mask;
+                const uint32_t l = st.q[i] & mask, hh = (st.q[i] >> 4) & mask;
                 lo[4 * i + 0] = fmaf(ubyte_f32<0>(l), dv, m8d);
                 lo[4 * i + 1] = fmaf(ubyte_f32<1>(l), dv, m8d);
                 lo[4 * i + 2] = fmaf(ubyte_f32<2>(l), dv, m8d);
                 lo[4 * i + 3] = fmaf(ubyte_f32<3>(l), dv, m8d);
-                hi[4 * i + 0] = fmaf(ubyte_f32<0>(h), dv, m8d);
-                hi[4 * i + 1] = fmaf(ubyte_f32<1>(h), dv, m8d);
-                hi[4 * i + 2] = fmaf(ubyte_f32<2>(h), dv, m8d);
-                hi[4 * i + 3] = fmaf(ubyte_f32<3>(h), dv, m8d);
+                hi[4 * i + 0] = fmaf(ubyte_f32<0>(hh), dv, m8d);
+                hi[4 * i + 1] = fmaf(ubyte_f32<1>(hh), dv, m8d);
+                hi[4 * i + 2] = fmaf(ubyte_f32<2>(hh), dv, m8d);
+                hi[4 * i + 3] = fmaf(ubyte_f32<3>(hh), dv, m8d);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o0[i] = pk_bf16(lo[2 * i], lo[2 * i + 1]);   // elements 8H + 2i..
-                o1[i] = pk_bf16(hi[2 * i], hi[2 * i + 1]);   // elements 16 + 8H + 2i..
-            }
+            *reinterpret_cast<uint4*>(row + 8 * h) =
+                make_uint4(pk_bf16(lo[0], lo[1]), pk_bf16(lo[2], lo[3]), pk_bf16(lo[4], lo[5]),
+                           pk_bf16(lo[6], lo[7]));
+            *reinterpret_cast<uint4*>(row + 16 + 8 * h) =
+                make_uint4(pk_bf16(hi[0], hi[1]), pk_bf16(hi[2], hi[3]), pk_bf16(hi[4], hi[5]),
+                           pk_bf16(hi[6], hi[7]));
         } else {
             // w = q d = fma(q + 128, d, -128 d): one rounding of the exact q d
             const float m128d = -128.f * dv;
-            const uint4 a = st.q[H];  // elements 16H .. 16H + 15
-            const uint32_t w[4] = {a.x ^ 0x80808080u, a.y ^ 0x80808080u, a.z ^ 0x80808080u,
-                                   a.w ^ 0x80808080u};
             uint32_t o[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                o[2 * i] = pk_bf16(fmaf(ubyte_f32<0>(w[i]), dv, m128d), fmaf(ubyte_f32<1>(w[i]), dv, m128d));
-                o[2 * i + 1] = pk_bf16(fmaf(ubyte_f32<2>(w[i]), dv, m128d), fmaf(ubyte_f32<3>(w[i]), dv, m128d));
+                const uint32_t w = st.q[i] ^ 0x80808080u;
+                o[2 * i] = pk_bf16(fmaf(ubyte_f32<0>(w), dv, m128d), fmaf(ubyte_f32<1>(w), dv, m128d));
+                o[2 * i + 1] = pk_bf16(fmaf(ubyte_f32<2>(w), dv, m128d), fmaf(ubyte_f32<3>(w), dv, m128d));
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o0[i] = o[i];
-                o1[i] = o[4 + i];
-            }
-        }
-        const int r = tid >> 1, b = tid & 1;
-        __bf16* row = &ws[r * LDK + 32 * b];
-        if constexpr (WT == kQ4) {
-            *reinterpret_cast<uint4*>(row + 8 * H) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-            *reinterpret_cast<uint4*>(row + 16 + 8 * H) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
-        } else {
-            *reinterpret_cast<uint4*>(row + 16 * H) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-            *reinterpret_cast<uint4*>(row + 16 * H + 8) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+            *reinterpret_cast<uint4*>(row + 16 * h) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(row + 16 * h + 8) = make_uint4(o[4], o[5], o[6], o[7]);
         }
     }
 }
 
 template <uint32_t WT, bool SF16>
-__device__ __forceinline__ void store_stage(const Stage<WT>& st, __bf16* __restrict__ xs,
-                                            __bf16* __restrict__ ws, int tid) {
-    store_part<WT, SF16, 0>(st, xs, ws, tid);
-    store_part<WT, SF16, 1>(st, xs, ws, tid);
-    store_part<WT, SF16, 2>(st, xs, ws, tid);
-    store_part<WT, SF16, 3>(st, xs, ws, tid);
-}
-
-template <uint32_t WT, bool SF16>
-__global__ __launch_bounds__(256) void gemm_big_kernel(
+__global__ __launch_bounds__(NT) void gemm_big_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ d, const uint16_t* __restrict__ x,
     float* __restrict__ y, float* __restrict__ ws_partial, uint32_t M, uint32_t N, uint32_t K,
     uint32_t k_per_split) {
@@ -376,7 +368,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 Xs[2][BM * LDK];
     __shared__ __attribute__((aligned(16))) __bf16 Ws[2][BN * LDK];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
+    const int grp = wid >> 2;                    // which k slices: 2 grp, 2 grp + 1 ... (see below)
+    const int wm = (wid >> 1) & 1, wn = wid & 1;
     Ctx<WT, SF16> c;
     c.M = M; c.N = N; c.K = K; c.tid = tid;
     c.m0 = blockIdx.y * BM;
@@ -399,17 +392,16 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(
     Stage<WT> sa, sb;
     c.fetch(kb, sa);
     c.fetch(kb + BK, sb);
-    store_stage<WT, SF16>(sa, Xs[0], Ws[0], tid);
+    store_part<WT, SF16, 0>(sa, Xs[0], Ws[0], tid);
+    store_part<WT, SF16, 1>(sa, Xs[0], Ws[0], tid);
     __syncthreads();
 
-    // One step: the 4 k slices of MFMAs on LDS buffer `cur`, with the
-    // store of the next step's data (register set `nx`) into the other buffer
-    // split into four parts between them.
+    // One step: this group's two k slices (16 grp and 32 + 16 grp) of MFMAs
+    // on LDS buffer `cur`, with the two store parts of the next step's data
+    // (register set nx) into the other buffer between them.
     auto step = [&](int cur, const Stage<WT>& nx) {
         const __bf16* __restrict__ xs = Xs[cur];
         const __bf16* __restrict__ wsb = Ws[cur];
-        __bf16* __restrict__ xn = Xs[cur ^ 1];
-        __bf16* __restrict__ wn_ = Ws[cur ^ 1];
         bf16x8 a[2][TM], b[2][TN];
         auto frags = [&](int kk, int set) {
             const int kc = kk + 8 * (lane >> 5);
@@ -427,18 +419,12 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[set][i], b[set][j], acc[i][j], 0, 0, 0);
         };
-        frags(0, 0);
-        frags(16, 1);
+        frags(16 * grp, 0);
+        frags(32 + 16 * grp, 1);
         mm(0);
-        store_part<WT, SF16, 0>(nx, xn, wn_, tid);
-        frags(32, 0);
+        store_part<WT, SF16, 0>(nx, Xs[cur ^ 1], Ws[cur ^ 1], tid);
         mm(1);
-        store_part<WT, SF16, 2>(nx, xn, wn_, tid);
-        frags(48, 1);
-        mm(0);
-        store_part<WT, SF16, 1>(nx, xn, wn_, tid);
-        mm(1);
-        store_part<WT, SF16, 3>(nx, xn, wn_, tid);
+        store_part<WT, SF16, 1>(nx, Xs[cur ^ 1], Ws[cur ^ 1], tid);
     };
 
     // Step s reads LDS[s & 1]; sa/sb alternate as the register set of step
@@ -457,6 +443,35 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(
         k0 += 2 * BK;
         if (k0 >= c.ke) break;
     }
+
+    // ---- add group 1's sums into group 0's through LDS (the stage buffers
+    // are free now), two tile columns at a time ----
+    float* red = reinterpret_cast<float*>(&Xs[0][0]);  // 4 waves x 4 tiles x 16 x 64 floats
+    const int wq = wid & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 2 * half; i < 2 * half + 2; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        red[(((wq * 4 + (i - 2 * half) * TN + j) * 16 + v) << 6) + lane] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 2 * half; i < 2 * half + 2; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[i][j][v] += red[(((wq * 4 + (i - 2 * half) * TN + j) * 16 + v) << 6) + lane];
+        }
+        __syncthreads();
+    }
+    if (grp == 1) return;
 
     // epilogue: lane holds column n = lane % 32, rows 8 (v / 4) + 4 (lane / 32) + v % 4
     float* out = ws_partial ? ws_partial + static_cast<uint64_t>(blockIdx.z) * M * N : y;
@@ -578,17 +593,17 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
         const uint16_t* xb = static_cast<const uint16_t*>(x);
         if (m.wtype == kQ4) {
             if (m.scale_f16)
-                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, true>), grid, dim3(256), 0, s,
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, true>), grid, dim3(big::NT), 0, s,
                                    m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
             else
-                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, false>), grid, dim3(256), 0, s,
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ4, false>), grid, dim3(big::NT), 0, s,
                                    m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
         } else {
             if (m.scale_f16)
-                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, true>), grid, dim3(256), 0, s,
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, true>), grid, dim3(big::NT), 0, s,
                                    m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
             else
-                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, false>), grid, dim3(256), 0, s,
+                hipLaunchKernelGGL((big::gemm_big_kernel<kQ8, false>), grid, dim3(big::NT), 0, s,
                                    m.q, m.d, xb, y, part, batch, m.rows, m.cols, p.k_per_split);
         }
         hipError_t e = hipGetLastError();
