@@ -10,7 +10,8 @@ timed steps run as one captured HIP graph (launch overhead out of the way),
 bracketed by device synchronisation and HIP events on the launching stream.
 
 Default workload: Q4_0 GEMV, 4096 x 4096, f16 scales, batch 1.  Other
-workloads (--workload): q8_gemv_512, decode_layer, gemm_q4_14336x4096,
+workloads (--workload): q8_gemv_512, decode_layer (wq|wk|wv and w1|w3 grouped
+on their shared inputs), decode_layer_7 (one launch per matrix), gemm_q4_14336x4096,
 gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, and copy (a plain
 device copy, used to calibrate HBM byte counters).
 """
@@ -52,12 +53,14 @@ def workload(name):
     if name == "q8_gemv_512":
         return ("Q8_0 GEMV 512x512, f32 scales, batch 1", "gemv", 1,
                 [(0, Q8, 0, 512, 512)], 1)
-    if name == "decode_layer":
+    if name in ("decode_layer", "decode_layer_7"):
         mats = []
         for m, (_, cls, r, c) in enumerate(LAYER):
             mats.append((m, Q.qmv_class_wtype(Q4, 8 | 64, cls, 0), 1, r, c))
+        how = ("4 launches: wq|wk|wv and w1|w3 grouped on their shared inputs"
+               if name == "decode_layer" else "7 launches, one per matrix")
         return ("mixed decode layer (q8_mask 8|64: wv, w2 Q8_0; others Q4_0), "
-                "dim 4096, kv 1024, ffn 11008, f16 scales, batch 1", "gemv", 3, mats, 1)
+                f"dim 4096, kv 1024, ffn 11008, f16 scales, batch 1, {how}", "gemv", 3, mats, 1)
     if name == "gemm_q4_14336x4096":
         return ("prefill GEMM Q4_0 14336x4096 f16 scales x bf16 [512x4096]", "gemm", 4,
                 [(0, Q4, 1, 14336, 4096)], 512)
@@ -76,14 +79,33 @@ def workload(name):
     raise SystemExit(f"unknown workload {name}")
 
 
+# launches of the fused decode layer: indexes into LAYER (shared activations)
+LAYER_GROUPS = [(0, 1, 2), (3,), (4, 5), (6,)]
+
+
+def launch_groups(name, mats):
+    """Lists of matrix positions that share one launch and one x."""
+    if name == "decode_layer":
+        return [list(g) for g in LAYER_GROUPS]
+    return [[i] for i in range(len(mats))]
+
+
 def matrix_bytes(wt, sf, r, c):
     q = r * c if wt == Q8 else r * c // 2
     return q + (r * c // 32) * (2 if sf else 4)
 
 
-def step_work(kind, mats, batch):
-    """Algorithmic bytes and flops of one step."""
+def step_work(kind, mats, batch, groups=None):
+    """Algorithmic bytes and flops of one step (an activation vector shared
+    by a launch group is counted once)."""
     byts = flops = 0
+    if kind == "gemv" and groups is not None:
+        for g in groups:
+            byts += 4 * mats[g[0]][4] * batch
+        for _, wt, sf, r, c in mats:
+            byts += matrix_bytes(wt, sf, r, c) + 4 * r * batch
+            flops += 2 * r * c * batch
+        return byts, flops
     for _, wt, sf, r, c in mats:
         w = matrix_bytes(wt, sf, r, c)
         if kind == "gemv":
@@ -229,7 +251,8 @@ def main():
                           "ms_per_copy": ms, "GB/s": 2 * n / ms / 1e6}))
         return
 
-    step_bytes, step_flops = step_work(kind, mats, batch)
+    groups = launch_groups(args.workload, mats)
+    step_bytes, step_flops = step_work(kind, mats, batch, groups if kind == "gemv" else None)
     set_bytes = sum(matrix_bytes(wt, sf, r, c) for _, wt, sf, r, c in mats)
     ncopies = max(2, -(-ROTATE_BYTES // set_bytes))
     if kind == "embed":
@@ -252,8 +275,12 @@ def main():
     log("weights uploaded")
 
     xs, ys = [], []
-    for (m, wt, sf, r, c) in mats:
-        g = synth.rng(config, m, synth.STREAM_ACT)
+    shared = kind == "gemv" and len(groups) < len(mats)
+    for pos, (m, wt, sf, r, c) in enumerate(mats):
+        # a launch group's matrices share one activation vector (the group's
+        # own seed stream); otherwise each matrix has its own
+        gi = [i for i, gr in enumerate(groups) if pos in gr][0] if kind == "gemv" else 0
+        g = synth.rng(config, 20 + gi if shared else m, synth.STREAM_ACT)
         if kind == "gemm":
             xb = synth.act_bf16(g, batch, c)
             xs.append(torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16))
@@ -270,6 +297,13 @@ def main():
 
     def step(i):
         hs = handles[i % ncopies]
+        if kind == "gemv":
+            for gr in groups:
+                if len(gr) == 1:
+                    Q.qmv_gemv(hs[gr[0]], xs[gr[0]], ys[gr[0]])
+                else:
+                    Q.qmv_gemv_group([hs[j] for j in gr], xs[gr[0]], [ys[j] for j in gr])
+            return
         for j, h in enumerate(hs):
             if kind == "gemv":
                 Q.qmv_gemv(h, xs[j], ys[j])
@@ -304,7 +338,7 @@ def main():
     ms_step = ms / steps
     log(f"timed {steps} steps: {ms:.3f} ms")
 
-    launches_per_step = len(mats)
+    launches_per_step = len(groups) if kind == "gemv" else len(mats)
     if kind == "gemm":
         value, unit = step_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
         bound, peak, runit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"

@@ -306,16 +306,18 @@ __device__ __forceinline__ void global_read_chunk(const float* __restrict__ xp, 
     }
 }
 
+// The one-shot product of workgroup `block` (blockIdx.x of a plain launch,
+// or the block's index within its matrix in a grouped launch).
 template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
+__device__ __forceinline__ void oneshot_body(
     const uint8_t* __restrict__ q, const void* __restrict__ d,
-    const float* __restrict__ x, float* __restrict__ y, uint32_t rows, uint32_t cols) {
+    const float* __restrict__ x, float* __restrict__ y, uint32_t rows, uint32_t cols,
+    uint32_t block, float4* __restrict__ smem) {
     constexpr int CW = (WT == kQ4) ? 32 : 16;   // weights per 16-byte chunk
     constexpr int G4 = CW / 4;
     constexpr int THREADS = WAVES * 64;
     constexpr float OFF = (WT == kQ4) ? 8.f : 128.f;
     constexpr uint32_t SB = SF16 ? 2 : 4;       // bytes per scale
-    extern __shared__ float4 smem[];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const uint32_t nchunks = cols / CW;
     const uint32_t S = (nchunks + 63) / 64;     // <= SMAX (host-checked)
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
     // ---- 2. every quant chunk and scale of this wave's rows ----
     const uint64_t row_bytes = (WT == kQ4) ? (cols >> 1) : cols;
     const uint32_t nblk = cols >> 5;
-    const uint32_t row0 = (blockIdx.x * WAVES + wid) * NR;
+    const uint32_t row0 = (block * WAVES + wid) * NR;
     const uint32_t wrows = row0 < rows ? min(static_cast<uint32_t>(NR), rows - row0) : 0;
     const uint32_t rb = min(row0, rows - 1);
     const __amdgpu_buffer_rsrc_t qrs =
@@ -426,6 +428,50 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
         }
 }
 
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
+    const uint8_t* __restrict__ q, const void* __restrict__ d,
+    const float* __restrict__ x, float* __restrict__ y, uint32_t rows, uint32_t cols) {
+    extern __shared__ float4 smem[];
+    oneshot_body<WT, SF16, NR, NB, SMAX, WAVES>(q, d, x, y, rows, cols, blockIdx.x, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped launch: several matrices with the same number of columns multiply
+// the same activations in one launch (a decode layer's wq | wk | wv, or
+// w1 | w3).  Workgroups [first[i], first[i+1]) serve matrix i with the
+// one-shot body of its own storage type, one row per wave.  One launch
+// instead of several saves each extra launch's fixed start-up and drain.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxGroup = 8;
+
+struct GroupArgs {
+    const uint8_t* q[kMaxGroup];
+    const void* d[kMaxGroup];
+    float* y[kMaxGroup];
+    uint32_t rows[kMaxGroup];
+    uint32_t kind[kMaxGroup];        // 2 * (wtype == Q8_0) + scale_f16
+    uint32_t first[kMaxGroup + 1];   // first workgroup of each matrix
+    uint32_t n;
+};
+
+template <int NB, int SMAX4, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_group_kernel(GroupArgs g,
+                                                                 const float* __restrict__ x,
+                                                                 uint32_t cols) {
+    extern __shared__ float4 smem[];
+    uint32_t i = 0;
+    while (i + 1 < g.n && blockIdx.x >= g.first[i + 1]) ++i;  // uniform
+    const uint32_t blk = blockIdx.x - g.first[i];
+    switch (g.kind[i]) {
+        case 0: oneshot_body<kQ4, false, 1, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        case 1: oneshot_body<kQ4, true, 1, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        case 2: oneshot_body<kQ8, false, 1, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        default: oneshot_body<kQ8, true, 1, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+    }
+}
+
 template <uint32_t WT, bool SF16, int NR, int NB>
 hipError_t gemv_launch(const MatView& m, const float* x, float* y, hipStream_t s) {
     const uint32_t waves = (m.rows + NR - 1) / NR;
@@ -510,11 +556,74 @@ hipError_t gemv_batched(const MatView& m, const float* x, float* y,
     return hipSuccess;
 }
 
+template <int NB>
+hipError_t group_pass(const MatView* ms, uint32_t n, const float* x, float* const* ys,
+                      uint32_t done, hipStream_t s) {
+    constexpr int WAVES = 8;
+    const uint32_t cols = ms[0].cols;
+    const uint32_t S4 = (cols / 32 + 63) / 64;
+    GroupArgs g{};
+    g.n = n;
+    uint32_t blocks = 0;
+    uint64_t lds = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        g.q[i] = ms[i].q;
+        g.d[i] = ms[i].d;
+        g.y[i] = ys[i] + static_cast<uint64_t>(done) * ms[i].rows;
+        g.rows[i] = ms[i].rows;
+        g.kind[i] = 2 * (ms[i].wtype == kQ8) + ms[i].scale_f16;
+        g.first[i] = blocks;
+        blocks += (ms[i].rows + WAVES - 1) / WAVES;
+        const uint64_t b = ms[i].wtype == kQ4 ? gemv_lds_bytes<kQ4>(cols, NB) : gemv_lds_bytes<kQ8>(cols, NB);
+        lds = b > lds ? b : lds;
+    }
+    g.first[n] = blocks;
+    const float* xp = x + static_cast<uint64_t>(done) * cols;
+    const size_t l = static_cast<size_t>(lds);
+    if (S4 <= 1) hipLaunchKernelGGL((gemv_group_kernel<NB, 1, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
+    else if (S4 <= 2) hipLaunchKernelGGL((gemv_group_kernel<NB, 2, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
+    else if (S4 <= 4) hipLaunchKernelGGL((gemv_group_kernel<NB, 4, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
+    else hipLaunchKernelGGL((gemv_group_kernel<NB, 8, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Batches up to this size run the vector kernel; larger ones the matrix
 // cores (each vector pass re-reads the whole matrix).
 constexpr uint32_t kGemvMaxBatch = 8;
+
+hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, float* const* ys,
+                             uint32_t batch, hipStream_t s) {
+    const uint32_t cols = ms[0].cols;
+    const uint32_t S4 = (cols / 32 + 63) / 64;
+    bool fits = n <= static_cast<uint32_t>(kMaxGroup) && batch <= kGemvMaxBatch && S4 <= 8;
+    for (uint32_t i = 0; fits && i < n; ++i) {
+        const uint64_t row_bytes = ms[i].wtype == kQ4 ? cols / 2 : cols;
+        const uint64_t lds = ms[i].wtype == kQ4 ? gemv_lds_bytes<kQ4>(cols, 1) : gemv_lds_bytes<kQ8>(cols, 1);
+        fits = lds * (batch > 4 ? 8 : batch > 2 ? 4 : batch) <= 64 * 1024 && row_bytes < 0xFFFFFFF0ull;
+    }
+    if (!fits) {  // one launch per matrix
+        for (uint32_t i = 0; i < n; ++i) {
+            const hipError_t e = launch_gemv(ms[i], x, ys[i], batch, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    uint32_t done = 0;
+    while (done < batch) {
+        const uint32_t left = batch - done;
+        hipError_t e;
+        uint32_t nb;
+        if (left >= 8) { nb = 8; e = group_pass<8>(ms, n, x, ys, done, s); }
+        else if (left >= 4) { nb = 4; e = group_pass<4>(ms, n, x, ys, done, s); }
+        else if (left >= 2) { nb = 2; e = group_pass<2>(ms, n, x, ys, done, s); }
+        else { nb = 1; e = group_pass<1>(ms, n, x, ys, done, s); }
+        if (e != hipSuccess) return e;
+        done += nb;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
                        uint32_t batch, hipStream_t s) {

@@ -17,6 +17,11 @@ struct MatView {
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
                        uint32_t batch, hipStream_t stream);
 
+// One launch for n <= 8 matrices with the same cols multiplying the same x:
+// ys[i] = W_i x (falls back to one launch per matrix when they do not fit).
+hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, float* const* ys,
+                             uint32_t batch, hipStream_t stream);
+
 // Same product on the matrix cores: x is bf16 bits, or f32 split into two
 // bf16 terms (x_f32 = true).  Large batches may split K; the slices' partial
 // sums then go to `workspace` (gemm_workspace_bytes of them; ignored when

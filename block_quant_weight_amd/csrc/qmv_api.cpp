@@ -160,6 +160,23 @@ int qmv_gemv(qmv_handle h, const float* x, float* y, uint32_t batch,
                                           static_cast<hipStream_t>(stream)));
 }
 
+int qmv_gemv_group(const qmv_handle* hs, uint32_t n, const float* x, float* const* ys,
+                   uint32_t batch, void* stream) {
+    if (hs == nullptr || ys == nullptr || x == nullptr || n == 0 || n > 8 || batch == 0)
+        return QMV_E_ARG;
+    if (!aligned16(x)) return QMV_E_ARG;
+    qmv::MatView ms[8];
+    for (uint32_t i = 0; i < n; ++i) {
+        const int st = ready(hs[i]);
+        if (st != QMV_OK) return st;
+        if (ys[i] == nullptr || !aligned16(ys[i])) return QMV_E_ARG;
+        ms[i] = view(hs[i]);
+        if (ms[i].cols != ms[0].cols) return QMV_E_SHAPE;
+    }
+    return device_status(qmv::launch_gemv_group(ms, n, x, ys, batch,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
              void* stream) {
     int st = ready(h);

@@ -21,7 +21,7 @@ QMV_E_NOMEM = -5
 
 # every symbol include/qmv.h declares
 EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
-           "qmv_destroy", "qmv_gemv", "qmv_gemm", "qmv_embed_rows",
+           "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str")
 
 _lib = None
@@ -49,6 +49,7 @@ def lib():
             "qmv_upload": ([vp, vp, u64, vp], i32),
             "qmv_destroy": ([vp], i32),
             "qmv_gemv": ([vp, vp, vp, u32, vp], i32),
+            "qmv_gemv_group": ([vp, u32, vp, vp, u32, vp], i32),
             "qmv_gemm": ([vp, vp, vp, u32, vp], i32),
             "qmv_embed_rows": ([vp, vp, u32, vp, vp], i32),
             "qmv_quantize_q8": ([vp, u64, vp, vp, vp], i32),
@@ -154,6 +155,25 @@ def qmv_gemv(h: QmvHandle, x, y, batch=None, stream=None):
     px = _dev(x, torch.float32, b * h.cols, "x")
     py = _dev(y, torch.float32, b * h.rows, "y")
     _check(lib().qmv_gemv(h.ptr, px, py, b, _stream(stream)), "qmv_gemv")
+
+
+def qmv_gemv_group(hs, x, ys, batch=None, stream=None):
+    """hs: list of handles with the same cols; x: float32 [batch, cols] on the
+    GPU; ys: list of float32 [batch, rows_i] GPU tensors."""
+    import torch
+    if len(hs) != len(ys):
+        raise ValueError("one output per handle")
+    cols = hs[0].cols
+    b = x.shape[0] if (batch is None and x.dim() == 2) else (batch or 1)
+    px = _dev(x, torch.float32, b * cols, "x")
+    n = len(hs)
+    harr = (ctypes.c_void_p * n)(*[h.ptr.value if isinstance(h.ptr, ctypes.c_void_p) else h.ptr
+                                   for h in hs])
+    yarr = (ctypes.c_void_p * n)(*[_dev(y, torch.float32, b * h.rows, f"ys[{i}]").value
+                                   for i, (h, y) in enumerate(zip(hs, ys))])
+    _check(lib().qmv_gemv_group(ctypes.cast(harr, ctypes.c_void_p), n, px,
+                                ctypes.cast(yarr, ctypes.c_void_p), b, _stream(stream)),
+           "qmv_gemv_group")
 
 
 def qmv_gemm(h: QmvHandle, x_bf16, y, batch=None, stream=None):

@@ -135,6 +135,21 @@ int qmv_gemv(qmv_handle h, const float *x, float *y, uint32_t batch,
              void *stream);
 
 /*
+ * Grouped decode product: n (1..8) matrices with the same cols, multiplying
+ * the same activations, in one launch: ys[i][t][r] = sum_c W_i[r][c] x[t][c].
+ * This is how a decode layer's matrices that share an input run (wq, wk, wv;
+ * w1, w3 — the .mlb page's body order), and it saves the fixed start-up and
+ * drain of every launch after the first.  hs: n handles (any mix of Q4_0 /
+ * Q8_0 and scale types); x: float32 [batch][cols]; ys: a host array of n
+ * device pointers, float32 [batch][rows_i].  Each output is what qmv_gemv
+ * would compute for that matrix, within the same bound.
+ * Errors: QMV_E_ARG (n not in 1..8, null or misaligned pointer, batch 0, a
+ * handle not uploaded), QMV_E_SHAPE (cols differ), QMV_E_DEVICE.
+ */
+int qmv_gemv_group(const qmv_handle *hs, uint32_t n, const float *x,
+                   float *const *ys, uint32_t batch, void *stream);
+
+/*
  * Prefill product (GEMM), y[t][r] = sum_c W[r][c] * x[t][c], with x given
  * as bfloat16 bit patterns: x_bf16 uint16 [batch][cols], y float32
  * [batch][rows], device memory.  Tiles of W are decoded to bfloat16

@@ -282,3 +282,46 @@ def test_gemm_split_k_is_deterministic():
         close(a[:, sel], ref, norm, "split-K gemm")
     finally:
         Q.qmv_destroy(h)
+
+
+def test_gemv_group_mixed_types_against_oracle_and_single():
+    # one launch over matrices of different storage types sharing x; each
+    # output equals the single-matrix product bit for bit (same arithmetic)
+    import torch
+    C = 1056
+    specs = [(2, 1, 300), (1, 1, 77), (2, 0, 129), (1, 0, 1)]
+    imgs, hs = [], []
+    try:
+        for m, (wt, sf, R) in enumerate(specs):
+            img = K.make_image(800, m, wt, sf, R, C, lo=-1e-2)
+            imgs.append(img)
+            hs.append(K.upload(img, wt, sf, R, C))
+        for batch in (1, 3, 8):
+            x = K.make_x(800, 10 + batch, batch, C)
+            xd = K.dev(x)
+            ys = [torch.empty((batch, R), dtype=torch.float32, device="cuda") for (_, _, R) in specs]
+            Q.qmv_gemv_group(hs, xd, ys)
+            torch.cuda.synchronize()
+            for (wt, sf, R), img, h, y in zip(specs, imgs, hs, ys):
+                yg = y.cpu().numpy()
+                ref, norm = O.product(img, wt, sf, R, C, x, threads=K.THREADS)
+                close(yg, ref, norm, f"group {wt}/{sf} {R}x{C} b{batch}")
+                assert np.array_equal(yg.view(np.uint32), K.gpu_gemv(h, x).view(np.uint32))
+    finally:
+        for h in hs:
+            Q.qmv_destroy(h)
+
+
+def test_gemv_group_rejects_mismatched_cols():
+    import torch
+    a = K.upload(K.make_image(801, 0, 2, 1, 64, 128), 2, 1, 64, 128)
+    b = K.upload(K.make_image(801, 1, 2, 1, 64, 256), 2, 1, 64, 256)
+    try:
+        x = torch.zeros((1, 256), dtype=torch.float32, device="cuda")
+        ys = [torch.zeros((1, 64), dtype=torch.float32, device="cuda") for _ in range(2)]
+        with pytest.raises(Q.QmvError) as e:
+            Q.qmv_gemv_group([a, b], x, ys)
+        assert e.value.status == Q.QMV_E_SHAPE
+    finally:
+        Q.qmv_destroy(a)
+        Q.qmv_destroy(b)

@@ -66,6 +66,31 @@ def test_mixed_decode_layer():
             Q.qmv_destroy(h)
 
 
+def test_mixed_decode_layer_fused_launches():
+    # the layer as it runs: wq | wk | wv share the attention input, wo its
+    # own, w1 | w3 share the FFN input, w2 its own: four launches
+    import torch
+    hs, imgs = {}, {}
+    try:
+        for m, (name, cls, R, C) in enumerate(K.LAYER):
+            wt = Q.qmv_class_wtype(K.Q4, K.LAYER_Q8_MASK, cls, 0)
+            imgs[name] = (K.make_image(3, m, wt, 1, R, C), wt, R, C)
+            hs[name] = K.upload(imgs[name][0], wt, 1, R, C)
+        for group, xm in ((("wq", "wk", "wv"), 20), (("wo",), 21), (("w1", "w3"), 22), (("w2",), 23)):
+            C = imgs[group[0]][3]
+            x = K.make_x(3, xm, 1, C)
+            ys = [torch.empty((1, imgs[n][2]), dtype=torch.float32, device="cuda") for n in group]
+            Q.qmv_gemv_group([hs[n] for n in group], K.dev(x), ys)
+            torch.cuda.synchronize()
+            for n, y in zip(group, ys):
+                img, wt, R, C = imgs[n]
+                ref, norm = O.product(img, wt, 1, R, C, x, threads=K.THREADS)
+                close(y.cpu().numpy(), ref, norm, f"fused layer {n}")
+    finally:
+        for h in hs.values():
+            Q.qmv_destroy(h)
+
+
 @pytest.mark.parametrize("which", ["q4_14336x4096", "q8_4096x14336"])
 def test_prefill_gemm_512_tokens(which):
     if which == "q4_14336x4096":
