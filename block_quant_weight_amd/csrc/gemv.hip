@@ -254,56 +254,192 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// One-shot kernel: every load of a wave is requested at entry.
+// One-shot kernel with integer block dot products.
 //
-// A wave owns NR rows and reads all S <= SMAX steps of each (lane l takes
-// chunks l, l + 64, ...).  Order of requests:
-//   1. the thread's first activation chunk (for the workgroup's LDS copy),
-//   2. every quant chunk and scale of the wave's rows (raw buffer loads; a
-//      step past the row's end gets an out-of-range offset: zeros, no
-//      traffic, and no branch around the load),
-//   3. the rest of the activation chunks, if any.
-// Then the activations go to LDS in a lane-permuted order (float4 g of
-// chunk l + 64k at ((k*G4 + g)*64 + l), so a wave reading step k touches 64
-// consecutive 16-byte slots), each with its chunk sum computed in the dot
-// product's element order; one barrier; then the rows are multiplied as
-// their quants arrive (loads complete in issue order).
+// Activations as digits.  A workgroup first converts the activations, per
+// block of 32 consecutive values (the span of one weight scale): with E the
+// binary exponent of the block's largest magnitude (amax in [2^(E-1), 2^E)),
+// each value becomes the integer X = rne(x * 2^(22-E)), |X| <= 2^22, so x is
+// kept to within 2^(E-23) <= amax * 2^-22.  X is split into three signed
+// base-256 digits, X = D0 + 256 D1 + 65536 D2 with Dk in [-128, 127], and
+// each digit plane is stored as packed int8, so that v_dot4_i32_i8 multiplies
+// four weight codes by four digits exactly.  A block then adds
+//     d * 2^(E-22) * (T0 + 256 T1 + 65536 T2),   Tk = sum_j v_j Dk_j,
+// to its row, where the Tk are exact int32 sums (|Tk| < 2^18) and the blocks
+// are accumulated in float32.  Q8_0 quants are used as they are (signed
+// int8); a Q4_0 nibble n enters as the unsigned byte n and the -8 offset as
+// the exact starting value -8 * sum_j Dk_j of each Tk.  Zero weights give
+// exactly zero; a non-finite activation makes its block's scale NaN.
+//
+// Work split: one wavefront owns NR consecutive rows; lane l reads the 16-byte
+// chunks l, l + 64, ... of each row (a Q4_0 chunk is a whole block, a Q8_0
+// chunk half a block).  Order of requests at entry:
+//   1. the thread's share of the activations (16 values per half block),
+//   2. every scale, then every quant chunk of the wave's rows (raw buffer
+//      loads; a step past the row's end gets an out-of-range offset: zeros,
+//      no traffic, and no branch around the load),
+// then the digit conversion into LDS, one barrier, and the rows are multiplied
+// as their quants arrive (loads complete in issue order).
+//
+// LDS layout per activation vector, for chunk c = l + 64k:
+//   digit piece p (16 bytes = 16 digits of one plane) at ((k*P + p)*64 + l),
+//     Q4_0: P = 6, piece 2*plane + half; Q8_0: P = 3, piece = plane;
+//   then the block info at (k*64 + l): Q4_0 {-8*sum D0, -8*sum D1, -8*sum D2,
+//   2^(E-22)} as 16 bytes, Q8_0 2^(E-22) as 4 bytes.
+// A wave reading step k touches 64 consecutive 16-byte slots.
 // ---------------------------------------------------------------------------
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOob = 0xFFFFFFF0u;  // an offset past any buffer's end
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
-    const uint32_t n = bytes > 0xFFFFFFF0ull ? 0xFFFFFFF0u : static_cast<uint32_t>(bytes);
+// A raw buffer descriptor over [base, base + bytes).  The launchers make
+// sure a wave's range stays below 2^32 - 16 bytes (the out-of-range offset),
+// so the size is computed in 32 bits: a 64-bit compare here would be done in
+// vector registers and make the compiler wait for outstanding loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                             static_cast<int>(n), 0x00020000);
+                                             static_cast<int>(bytes), 0x00020000);
 }
 
-template <int CW>
-__device__ __forceinline__ void lds_read_x(const float4* __restrict__ xl, uint32_t k, int lane,
-                                           float (&xs)[CW]) {
-    constexpr int G4 = CW / 4;
+template <uint32_t WT>
+struct DigitLayout {
+    static constexpr int CW = (WT == kQ4) ? 32 : 16;   // weights per 16-byte chunk
+    static constexpr int P = (WT == kQ4) ? 6 : 3;      // digit pieces per chunk
+    static constexpr int INFO = (WT == kQ4) ? 16 : 4;  // info bytes per chunk
+    // bytes of one staged activation vector with S steps of 64 chunks
+    static __host__ __device__ uint32_t vector_bytes(uint32_t S) {
+        return S * 64 * (P * 16 + INFO);
+    }
+};
+
+__device__ __forceinline__ int dpp_swap_pair_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+}
+
+// Bytes [b0 b1 b2 .] of four words -> the three planes {b_k of w0..w3}.
+__device__ __forceinline__ void transpose3(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                           uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+    // v_perm_b32: selector byte s picks byte s of the 64-bit {src0:src1}
+    // (0..3 from src1, 4..7 from src0)
+    const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
+    const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x06020602u);  // w0.2 w1.2 (twice)
+    const uint32_t c = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
+    const uint32_t e = __builtin_amdgcn_perm(w3, w2, 0x06020602u);  // w2.2 w3.2 (twice)
+    p0 = __builtin_amdgcn_perm(c, a, 0x05040100u);                   // w0.0 w1.0 w2.0 w3.0
+    p1 = __builtin_amdgcn_perm(c, a, 0x07060302u);                   // w0.1 w1.1 w2.1 w3.1
+    p2 = __builtin_amdgcn_perm(e, b, 0x05040100u);                   // w0.2 w1.2 w2.2 w3.2
+}
+
+// Converts half block j (16 activations in xv; j even = first half) and
+// stores its digit pieces and, from the even lane, its block info.  The two
+// halves of a block sit in adjacent lanes of one wave, which exchange their
+// largest magnitude and digit sums.  `dig` and `info` point at the vector's
+// LDS area; h is the half block's index within its vector.
+template <uint32_t WT>
+__device__ __forceinline__ void stage_half(const float4 (&xv)[4], uint32_t h,
+                                           int4* __restrict__ dig, void* __restrict__ info) {
+    using L = DigitLayout<WT>;
+    const float v[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
+                         xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
+    // largest magnitude as an integer maximum of the absolute bit patterns,
+    // so that inf and NaN win over every finite value
+    uint32_t m = 0;
 #pragma unroll
-    for (int g = 0; g < G4; ++g) {
-        const float4 t = xl[(k * G4 + g) * 64 + lane];
-        xs[4 * g + 0] = t.x;
-        xs[4 * g + 1] = t.y;
-        xs[4 * g + 2] = t.z;
-        xs[4 * g + 3] = t.w;
+    for (int i = 0; i < 16; ++i) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
+    m = max(m, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(m))));
+    const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
+    const float sx = m >= 0x7F800000u ? __builtin_bit_cast(float, 0x7FC00000u)
+                                      : __builtin_amdgcn_ldexpf(1.0f, E - 22);
+    // X + 0x808080 in the low three bytes: rne(x * 2^(22-E)) by adding
+    // 1.5 * 2^23, whose bits are then 0x4B400000 + X
+    uint32_t u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float t = __builtin_amdgcn_ldexpf(v[i], 22 - E) + 12582912.0f;
+        u[i] = __builtin_bit_cast(uint32_t, t) - 0x4ABF7F80u;
+    }
+    uint32_t pl[3][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        transpose3(u[4 * g], u[4 * g + 1], u[4 * g + 2], u[4 * g + 3], pl[0][g], pl[1][g],
+                   pl[2][g]);
+#pragma unroll
+        for (int dd = 0; dd < 3; ++dd) pl[dd][g] ^= 0x80808080u;  // byte + 128 -> signed digit
+    }
+    if constexpr (WT == kQ4) {
+        const uint32_t c = h >> 1, half = h & 1, k = c >> 6, l = c & 63;
+#pragma unroll
+        for (int dd = 0; dd < 3; ++dd)
+            dig[(k * L::P + 2 * dd + half) * 64 + l] =
+                make_int4(pl[dd][0], pl[dd][1], pl[dd][2], pl[dd][3]);
+        int s[3];
+#pragma unroll
+        for (int dd = 0; dd < 3; ++dd) {
+            int a = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) a = __builtin_amdgcn_sdot4(pl[dd][g], 0x01010101, a, false);
+            s[dd] = a + dpp_swap_pair_i(a);
+        }
+        if (half == 0)
+            static_cast<int4*>(info)[k * 64 + l] =
+                make_int4(-8 * s[0], -8 * s[1], -8 * s[2], __builtin_bit_cast(int, sx));
+    } else {
+        const uint32_t c = h, k = c >> 6, l = c & 63;
+#pragma unroll
+        for (int dd = 0; dd < 3; ++dd)
+            dig[(k * L::P + dd) * 64 + l] = make_int4(pl[dd][0], pl[dd][1], pl[dd][2], pl[dd][3]);
+        static_cast<float*>(info)[k * 64 + l] = sx;
     }
 }
 
-template <int CW>
-__device__ __forceinline__ void global_read_chunk(const float* __restrict__ xp, float (&xs)[CW]) {
-    const float4* p = reinterpret_cast<const float4*>(xp);
+// T0 + 256 T1 + 65536 T2 in float32 (T1 + 256 T2 is exact in int32).
+__device__ __forceinline__ float combine_digits(int t0, int t1, int t2) {
+    const int hi = t1 + t2 * 256;
+    return fmaf(static_cast<float>(hi), 256.f, static_cast<float>(t0));
+}
+
+// Digit sums of one Q4_0 chunk (a whole block) with quants w.
+__device__ __forceinline__ float q4_digit_dot(const uint4 w, const int4 (&pc)[6], const int4 info) {
+    uint32_t mask = 0x0F0F0F0Fu;
+    asm("" : "+v"(mask));
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+    int t[3] = {info.x, info.y, info.z};
 #pragma unroll
-    for (int g = 0; g < CW / 4; ++g) {
-        const float4 t = p[g];
-        xs[4 * g + 0] = t.x;
-        xs[4 * g + 1] = t.y;
-        xs[4 * g + 2] = t.z;
-        xs[4 * g + 3] = t.w;
+    for (int dd = 0; dd < 3; ++dd) {
+        const int lo_d[4] = {pc[2 * dd].x, pc[2 * dd].y, pc[2 * dd].z, pc[2 * dd].w};
+        const int hi_d[4] = {pc[2 * dd + 1].x, pc[2 * dd + 1].y, pc[2 * dd + 1].z, pc[2 * dd + 1].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[dd] = __builtin_amdgcn_sdot4(static_cast<int>(q[i] & mask), lo_d[i], t[dd], false);
+            t[dd] = __builtin_amdgcn_sdot4(static_cast<int>((q[i] >> 4) & mask), hi_d[i], t[dd], false);
+        }
     }
+    return combine_digits(t[0], t[1], t[2]);
+}
+
+// Digit sums of one Q8_0 chunk (half a block) with quants w.
+__device__ __forceinline__ float q8_digit_dot(const uint4 w, const int4 (&pc)[3]) {
+    const int q[4] = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                      static_cast<int>(w.w)};
+    int t[3];
+#pragma unroll
+    for (int dd = 0; dd < 3; ++dd) {
+        const int dg[4] = {pc[dd].x, pc[dd].y, pc[dd].z, pc[dd].w};
+        int a = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_amdgcn_sdot4(q[i], dg[i], a, false);
+        t[dd] = a;
+    }
+    return combine_digits(t[0], t[1], t[2]);
+}
+
+// Half blocks of activations each thread loads before the quants: enough for
+// NB vectors of up to SMAX steps (at most 2; any rest is loaded afterwards).
+template <uint32_t WT, int NB, int SMAX, int WAVES>
+constexpr int stage_rounds() {
+    constexpr int halves = NB * SMAX * 64 * DigitLayout<WT>::CW / 16;
+    constexpr int r = (halves + WAVES * 64 - 1) / (WAVES * 64);
+    return r < 1 ? 1 : (r > 2 ? 2 : r);
 }
 
 // The one-shot product of workgroup `block` (blockIdx.x of a plain launch,
@@ -313,50 +449,51 @@ __device__ __forceinline__ void oneshot_body(
     const uint8_t* __restrict__ q, const void* __restrict__ d,
     const float* __restrict__ x, float* __restrict__ y, uint32_t rows, uint32_t cols,
     uint32_t block, float4* __restrict__ smem) {
-    constexpr int CW = (WT == kQ4) ? 32 : 16;   // weights per 16-byte chunk
-    constexpr int G4 = CW / 4;
+    using L = DigitLayout<WT>;
+    constexpr int CW = L::CW;
+    constexpr int P = L::P;
     constexpr int THREADS = WAVES * 64;
-    constexpr float OFF = (WT == kQ4) ? 8.f : 128.f;
+    constexpr int XR = stage_rounds<WT, NB, SMAX, WAVES>();
     constexpr uint32_t SB = SF16 ? 2 : 4;       // bytes per scale
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index in a scalar register, so that everything derived from
+    // it (row range, buffer descriptors) is known to be wave-uniform
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t nchunks = cols / CW;
     const uint32_t S = (nchunks + 63) / 64;     // <= SMAX (host-checked)
-    const uint32_t per_b = S * G4 * 64;          // float4 slots per vector
-    float4* xl = smem;
-    float* sxl = reinterpret_cast<float*>(smem + static_cast<size_t>(NB) * per_b);
+    const uint32_t nhalf = cols / 16;           // half blocks per vector
+    const uint32_t nstage = NB * nhalf;
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+    const uint32_t dig_bytes = S * P * 64 * 16;     // per vector
+    const uint32_t vec_bytes = L::vector_bytes(S);  // digits + info, per vector
 
-    // ---- 1. first activation chunk of this thread (b = 0.., chunk c) ----
-    const uint32_t nstage = NB * nchunks;       // chunks to stage
-    float xs0[CW];
-    if (static_cast<uint32_t>(tid) < nstage) {
-        const uint32_t b = tid / nchunks, c = tid - b * nchunks;
-        global_read_chunk<CW>(x + static_cast<uint64_t>(b) * cols + static_cast<uint64_t>(c) * CW,
-                              xs0);
+    // ---- 1. this thread's activations ----
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    float4 xr[XR][4];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        const uint32_t j = tid + i * THREADS;
+        if (j < nstage) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) xr[i][g] = x4[4ull * j + g];
+        }
     }
 
-    // ---- 2. every quant chunk and scale of this wave's rows ----
+    // ---- 2. every scale and quant chunk of this wave's rows ----
     const uint64_t row_bytes = (WT == kQ4) ? (cols >> 1) : cols;
     const uint32_t nblk = cols >> 5;
     const uint32_t row0 = (block * WAVES + wid) * NR;
     const uint32_t wrows = row0 < rows ? min(static_cast<uint32_t>(NR), rows - row0) : 0;
     const uint32_t rb = min(row0, rows - 1);
     const __amdgpu_buffer_rsrc_t qrs =
-        make_rsrc(q + static_cast<uint64_t>(rb) * row_bytes, static_cast<uint64_t>(wrows) * row_bytes);
+        make_rsrc(q + static_cast<uint64_t>(rb) * row_bytes, wrows * static_cast<uint32_t>(row_bytes));
     const __amdgpu_buffer_rsrc_t drs =
         make_rsrc(static_cast<const uint8_t*>(d) + static_cast<uint64_t>(rb) * nblk * SB,
-                  static_cast<uint64_t>(wrows) * nblk * SB);
+                  wrows * nblk * SB);
     uint4 qv[NR][SMAX];
     uint32_t dv[NR][SMAX];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-#pragma unroll
-        for (int k = 0; k < SMAX; ++k) {
-            const uint32_t ch = lane + 64 * k;
-            const uint32_t qo = ch < nchunks ? r * static_cast<uint32_t>(row_bytes) + 16 * ch : kOob;
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, qo, 0, 0);
-            qv[r][k] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-    }
+    // the small scale loads first: loads complete in issue order, so each
+    // step then waits for its own quants only
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
@@ -368,25 +505,33 @@ __device__ __forceinline__ void oneshot_body(
             else dv[r][k] = __builtin_amdgcn_raw_buffer_load_b32(drs, dofs, 0, 0);
         }
     }
-
-    // ---- 3. activations -> LDS with chunk sums ----
-    auto stage = [&](uint32_t j, const float (&xs)[CW]) {
-        const uint32_t b = j / nchunks, c = j - b * nchunks;
-        const uint32_t k = c >> 6, l = c & 63;
-        float4* dst = xl + b * per_b + (k * G4) * 64 + l;
 #pragma unroll
-        for (int g = 0; g < G4; ++g)
-            dst[g * 64] = make_float4(xs[4 * g], xs[4 * g + 1], xs[4 * g + 2], xs[4 * g + 3]);
-        float sx;
-        if constexpr (WT == kQ4) sx = q4_xsum(xs); else sx = q8_xsum(xs);
-        sxl[b * S * 64 + c] = sx;
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const uint32_t ch = lane + 64 * k;
+            const uint32_t qo = ch < nchunks ? r * static_cast<uint32_t>(row_bytes) + 16 * ch : kOob;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, qo, 0, 0);
+            qv[r][k] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+
+    // ---- 3. activations -> digits in LDS ----
+    auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
+        const uint32_t b = j / nhalf, h = j - b * nhalf;
+        uint8_t* base = lds + b * vec_bytes;
+        stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
     };
-    if (static_cast<uint32_t>(tid) < nstage) stage(tid, xs0);
-    for (uint32_t j = tid + THREADS; j < nstage; j += THREADS) {
-        float xs[CW];
-        const uint32_t b = j / nchunks, c = j - b * nchunks;
-        global_read_chunk<CW>(x + static_cast<uint64_t>(b) * cols + static_cast<uint64_t>(c) * CW, xs);
-        stage(j, xs);
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        const uint32_t j = tid + i * THREADS;
+        if (j < nstage) stage(j, xr[i]);
+    }
+    for (uint32_t j = tid + XR * THREADS; j < nstage; j += THREADS) {
+        float4 xv[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) xv[g] = x4[4ull * j + g];
+        stage(j, xv);
     }
     __syncthreads();
     if (wrows == 0) return;  // uniform per wave, after the barrier
@@ -400,20 +545,31 @@ __device__ __forceinline__ void oneshot_body(
 #pragma unroll
     for (int k = 0; k < SMAX; ++k) {
         if (k < static_cast<int>(S)) {
-            const uint32_t ch = lane + 64 * k;
-            const bool valid = ch < nchunks;
+            const bool valid = lane + 64u * k < nchunks;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                float xs[CW];
-                lds_read_x<CW>(xl + b * per_b, k, lane, xs);
-                const float sx = sxl[b * S * 64 + ch];
+                const uint8_t* base = lds + b * vec_bytes;
+                const int4* dg = reinterpret_cast<const int4*>(base) + k * P * 64 + lane;
+                int4 pc[P];
 #pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    float raw;
-                    if constexpr (WT == kQ4) raw = q4_raw_dot(qv[r][k], xs);
-                    else raw = q8_raw_dot(qv[r][k], xs);
-                    const float t = fmaf(scale_from_bits<SF16>(dv[r][k]), raw - OFF * sx, acc[b][r]);
-                    acc[b][r] = valid ? t : acc[b][r];
+                for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
+                if constexpr (WT == kQ4) {
+                    const int4 info = reinterpret_cast<const int4*>(base + dig_bytes)[k * 64 + lane];
+                    const float sx = __builtin_bit_cast(float, info.w);
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float t = q4_digit_dot(qv[r][k], pc, info);
+                        const float a = fmaf(scale_from_bits<SF16>(dv[r][k]) * sx, t, acc[b][r]);
+                        acc[b][r] = valid ? a : acc[b][r];
+                    }
+                } else {
+                    const float sx = reinterpret_cast<const float*>(base + dig_bytes)[k * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float t = q8_digit_dot(qv[r][k], pc);
+                        const float a = fmaf(scale_from_bits<SF16>(dv[r][k]) * sx, t, acc[b][r]);
+                        acc[b][r] = valid ? a : acc[b][r];
+                    }
                 }
             }
         }
@@ -437,14 +593,253 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Grouped launch: several matrices with the same number of columns multiply
-// the same activations in one launch (a decode layer's wq | wk | wv, or
-// w1 | w3).  Workgroups [first[i], first[i+1]) serve matrix i with the
-// one-shot body of its own storage type, one row per wave.  One launch
-// instead of several saves each extra launch's fixed start-up and drain.
+// Streaming kernel for large matrices: one workgroup of 16 waves per compute
+// unit converts the activations once, then each wave walks over row tiles
+// (NR rows each) t = w, w + W, w + 2W, ... of a list of matrices of one
+// storage type, with the loads of its next two tiles in flight while it
+// multiplies the current one.  The tile loop is branch-free around the
+// loads: a tile past the end gets an empty buffer range, so its loads return
+// zeros without memory traffic and the three register sets rotate in
+// straight-line code (loads complete in issue order, so each wait covers one
+// tile only).
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxGroup = 8;
+constexpr int kStreamWaves = 16;
+
+struct TileArgs {
+    const uint8_t* q[kMaxGroup];
+    const void* d[kMaxGroup];
+    float* y[kMaxGroup];
+    uint32_t rows[kMaxGroup];
+    uint32_t first[kMaxGroup + 1];   // first tile of each matrix; first[n] = all tiles
+    uint32_t n;
+};
+
+template <int NR, int SMAX>
+struct TileRegs {
+    uint4 q[NR][SMAX];
+    uint32_t d[NR][SMAX];
+    uint32_t mat, row0, wrows;      // wave-uniform
+};
+
+// Requests the scales, then the quants, of tile t (which may be past the end).
+template <uint32_t WT, bool SF16, int NR, int SMAX>
+__device__ __forceinline__ void load_tile(const TileArgs& g, uint32_t t, uint32_t cols,
+                                          uint32_t lane, uint32_t& mat, TileRegs<NR, SMAX>& b) {
+    constexpr uint32_t CW = DigitLayout<WT>::CW;
+    constexpr uint32_t SB = SF16 ? 2 : 4;
+    // matrix of tile t: the number of later matrices that start at or before
+    // t, in plain integer arithmetic (first[i] = 2^31 - 1 past the list), so
+    // that it stays in scalar registers: neither a loop nor a lane mask here,
+    // either of which makes the compiler wait for every outstanding load
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 1; i <= kMaxGroup; ++i)
+        m += 1u + static_cast<uint32_t>(static_cast<int32_t>(t - g.first[i]) >> 31);
+    mat = min(m, g.n - 1);
+    const bool live = t < g.first[g.n];
+    const uint32_t row0 = live ? (t - g.first[mat]) * NR : 0;
+    const uint32_t rows = g.rows[mat];
+    const uint32_t wrows = live ? min(static_cast<uint32_t>(NR), rows - row0) : 0;
+    const uint32_t nchunks = cols / CW;
+    const uint64_t row_bytes = (WT == kQ4) ? (cols >> 1) : cols;
+    const uint32_t nblk = cols >> 5;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(g.q[mat] + static_cast<uint64_t>(row0) * row_bytes,
+                  wrows * static_cast<uint32_t>(row_bytes));
+    const __amdgpu_buffer_rsrc_t drs =
+        make_rsrc(static_cast<const uint8_t*>(g.d[mat]) + static_cast<uint64_t>(row0) * nblk * SB,
+                  wrows * nblk * SB);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const uint32_t ch = lane + 64 * k;
+            const uint32_t blk = (WT == kQ4) ? ch : (ch >> 1);
+            const uint32_t dofs = ch < nchunks ? (r * nblk + blk) * SB : kOob;
+            if constexpr (SF16) b.d[r][k] = __builtin_amdgcn_raw_buffer_load_b16(drs, dofs, 0, 0);
+            else b.d[r][k] = __builtin_amdgcn_raw_buffer_load_b32(drs, dofs, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const uint32_t ch = lane + 64 * k;
+            const uint32_t qo = ch < nchunks ? r * static_cast<uint32_t>(row_bytes) + 16 * ch : kOob;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs, qo, 0, 0);
+            b.q[r][k] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    b.mat = mat;
+    b.row0 = row0;
+    b.wrows = wrows;
+}
+
+// Multiplies a loaded tile by the NB staged vectors and stores its rows.
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX>
+__device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<NR, SMAX>& b,
+                                             const uint8_t* __restrict__ lds, uint32_t cols,
+                                             uint32_t S, uint32_t lane) {
+    using L = DigitLayout<WT>;
+    constexpr int P = L::P;
+    const uint32_t nchunks = cols / L::CW;
+    const uint32_t dig_bytes = S * P * 64 * 16;
+    const uint32_t vec_bytes = L::vector_bytes(S);
+    float acc[NB][NR];
+#pragma unroll
+    for (int v = 0; v < NB; ++v)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[v][r] = 0.f;
+#pragma unroll
+    for (int k = 0; k < SMAX; ++k) {
+        if (k < static_cast<int>(S)) {
+            const bool valid = lane + 64u * k < nchunks;
+#pragma unroll
+            for (int v = 0; v < NB; ++v) {
+                const uint8_t* base = lds + v * vec_bytes;
+                const int4* dg = reinterpret_cast<const int4*>(base) + k * P * 64 + lane;
+                int4 pc[P];
+#pragma unroll
+                for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
+                if constexpr (WT == kQ4) {
+                    const int4 info = reinterpret_cast<const int4*>(base + dig_bytes)[k * 64 + lane];
+                    const float sx = __builtin_bit_cast(float, info.w);
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float t = q4_digit_dot(b.q[r][k], pc, info);
+                        const float a = fmaf(scale_from_bits<SF16>(b.d[r][k]) * sx, t, acc[v][r]);
+                        acc[v][r] = valid ? a : acc[v][r];
+                    }
+                } else {
+                    const float sx = reinterpret_cast<const float*>(base + dig_bytes)[k * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const float t = q8_digit_dot(b.q[r][k], pc);
+                        const float a = fmaf(scale_from_bits<SF16>(b.d[r][k]) * sx, t, acc[v][r]);
+                        acc[v][r] = valid ? a : acc[v][r];
+                    }
+                }
+            }
+        }
+    }
+    const uint32_t rows = g.rows[b.mat];
+    float* y = g.y[b.mat];
+#pragma unroll
+    for (int v = 0; v < NB; ++v)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float sum = wave_reduce(acc[v][r]);
+            if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
+                y[static_cast<uint64_t>(v) * rows + b.row0 + r] = sum;
+        }
+}
+
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int DEPTH>
+__global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
+    TileArgs g, const float* __restrict__ x, uint32_t cols, uint32_t per_wg) {
+    extern __shared__ float4 smem[];
+    using L = DigitLayout<WT>;
+    constexpr int THREADS = kStreamWaves * 64;
+    constexpr int XR = stage_rounds<WT, NB, SMAX, kStreamWaves>();
+    const int tid = threadIdx.x;
+    const uint32_t lane = tid & 63;
+    const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t S = (cols / L::CW + 63) / 64;
+    const uint32_t nhalf = cols / 16;
+    const uint32_t nstage = NB * nhalf;
+    uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
+    const uint32_t dig_bytes = S * L::P * 64 * 16;
+    const uint32_t vec_bytes = L::vector_bytes(S);
+    // tiles of this wave: t0, t0 + step, ... below `end`; per_wg = 0 spreads
+    // the tiles over the whole grid (t0 = global wave, step = all waves),
+    // otherwise workgroup b owns tiles [b * per_wg, (b + 1) * per_wg)
+    const uint32_t total = g.first[g.n];
+    uint32_t t, step, end;
+    if (per_wg == 0) {
+        t = blockIdx.x * kStreamWaves + wid;
+        step = gridDim.x * kStreamWaves;
+        end = total;
+    } else {
+        t = blockIdx.x * per_wg + wid;
+        step = kStreamWaves;
+        end = min(total, (blockIdx.x + 1) * per_wg);
+    }
+
+    // activations first, then the first tiles
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    float4 xr[XR][4];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        const uint32_t j = tid + i * THREADS;
+        if (j < nstage) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xr[i][c] = x4[4ull * j + c];
+        }
+    }
+    uint32_t mat = 0;
+    // tiles at or past `end` load nothing
+    auto tile = [&](uint32_t u) { return u < end ? u : 0xFFFFFFFEu; };
+    TileRegs<NR, SMAX> ra, rb, rc;
+    load_tile<WT, SF16, NR, SMAX>(g, tile(t), cols, lane, mat, ra);
+    if constexpr (DEPTH == 3) load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, rb);
+
+    auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
+        const uint32_t v = j / nhalf, h = j - v * nhalf;
+        uint8_t* base = lds + v * vec_bytes;
+        stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
+    };
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        const uint32_t j = tid + i * THREADS;
+        if (j < nstage) stage(j, xr[i]);
+    }
+    for (uint32_t j = tid + XR * THREADS; j < nstage; j += THREADS) {
+        float4 xv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xv[c] = x4[4ull * j + c];
+        stage(j, xv);
+    }
+    __syncthreads();
+
+    if constexpr (DEPTH == 3) {
+        // three register sets in rotation: the loads of the next two tiles
+        // are in flight while a tile is multiplied
+        while (t < end) {
+            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, rc);
+            compute_tile<WT, SF16, NR, NB, SMAX>(g, ra, lds, cols, S, lane);
+            t += step;
+            if (t >= end) break;
+            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, ra);
+            compute_tile<WT, SF16, NR, NB, SMAX>(g, rb, lds, cols, S, lane);
+            t += step;
+            if (t >= end) break;
+            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, rb);
+            compute_tile<WT, SF16, NR, NB, SMAX>(g, rc, lds, cols, S, lane);
+            t += step;
+        }
+    } else {
+        // two register sets: the next tile's loads are in flight
+        while (t < end) {
+            load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, rb);
+            compute_tile<WT, SF16, NR, NB, SMAX>(g, ra, lds, cols, S, lane);
+            t += step;
+            if (t >= end) break;
+            load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, ra);
+            compute_tile<WT, SF16, NR, NB, SMAX>(g, rb, lds, cols, S, lane);
+            t += step;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped launch: several matrices with the same number of columns multiply
+// the same activations in one launch (a decode layer's wq | wk | wv, or
+// w1 | w3).  Workgroups [first[i], first[i+1]) serve matrix i with the
+// one-shot body of its own storage type, NR rows per wave.  One launch
+// instead of several saves each extra launch's fixed start-up and drain.
+// ---------------------------------------------------------------------------
 
 struct GroupArgs {
     const uint8_t* q[kMaxGroup];
@@ -456,19 +851,20 @@ struct GroupArgs {
     uint32_t n;
 };
 
-template <int NB, int SMAX4, int WAVES>
+template <int NR, int NB, int SMAX4, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_group_kernel(GroupArgs g,
                                                                  const float* __restrict__ x,
                                                                  uint32_t cols) {
     extern __shared__ float4 smem[];
+    // the matrix of this workgroup (uniform; a short scalar search)
     uint32_t i = 0;
-    while (i + 1 < g.n && blockIdx.x >= g.first[i + 1]) ++i;  // uniform
+    while (i + 1 < g.n && blockIdx.x >= g.first[i + 1]) ++i;
     const uint32_t blk = blockIdx.x - g.first[i];
     switch (g.kind[i]) {
-        case 0: oneshot_body<kQ4, false, 1, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
-        case 1: oneshot_body<kQ4, true, 1, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
-        case 2: oneshot_body<kQ8, false, 1, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
-        default: oneshot_body<kQ8, true, 1, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        case 0: oneshot_body<kQ4, false, NR, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        case 1: oneshot_body<kQ4, true, NR, NB, SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        case 2: oneshot_body<kQ8, false, NR, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
+        default: oneshot_body<kQ8, true, NR, NB, 2 * SMAX4, WAVES>(g.q[i], g.d[i], x, g.y[i], g.rows[i], cols, blk, smem); break;
     }
 }
 
@@ -491,43 +887,129 @@ hipError_t gemv_oneshot_launch(const MatView& m, const float* x, float* y, size_
     return hipGetLastError();
 }
 
-// LDS bytes of the staged activations and their chunk sums.
+// The one-shot kernel's limits: at most 16 steps of 64 chunks per row, the
+// staged activations in at most this much LDS, and a wave's rows within a
+// 32-bit buffer range.
+constexpr uint64_t kOneshotLds = 64 * 1024;
+constexpr uint32_t kOneshotSteps = 16;
+
 template <uint32_t WT>
 uint64_t gemv_lds_bytes(uint32_t cols, uint32_t nb) {
-    constexpr uint32_t CW = (WT == kQ4) ? 32 : 16;
-    const uint64_t S = (cols / CW + 63) / 64;
-    return static_cast<uint64_t>(nb) * S * 64 * (CW + 1) * 4;
+    const uint32_t S = (cols / DigitLayout<WT>::CW + 63) / 64;
+    return static_cast<uint64_t>(nb) * DigitLayout<WT>::vector_bytes(S);
+}
+
+template <uint32_t WT>
+bool oneshot_fits(uint32_t cols, uint32_t nb, uint32_t nr) {
+    const uint32_t S = (cols / DigitLayout<WT>::CW + 63) / 64;
+    const uint64_t row_bytes = (WT == kQ4) ? cols / 2 : cols;
+    return S <= kOneshotSteps && gemv_lds_bytes<WT>(cols, nb) <= kOneshotLds &&
+           nr * row_bytes < 0xFFFFFFF0ull;
+}
+
+// Vectors per pass: the largest of 8, 4, 2, 1 that is left and whose staged
+// activations fit the one-shot kernel's LDS.
+template <uint32_t WT>
+uint32_t pass_vectors(uint32_t cols, uint32_t left) {
+    uint32_t nb = left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+    while (nb > 1 && gemv_lds_bytes<WT>(cols, nb) > kOneshotLds) nb /= 2;
+    return nb;
+}
+
+// Streaming launch over the matrices ms[0..n) (one storage type, one scale
+// type, the same cols), NR rows per tile, one workgroup per compute unit.
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX>
+hipError_t stream_launch(const MatView* ms, uint32_t n, const float* x, float* const* ys,
+                         uint32_t done, hipStream_t s) {
+    TileArgs g{};
+    g.n = n;
+    uint32_t tiles = 0;
+    for (uint32_t i = 0; i < n; ++i) {
+        g.q[i] = ms[i].q;
+        g.d[i] = ms[i].d;
+        g.y[i] = ys[i] + static_cast<uint64_t>(done) * ms[i].rows;
+        g.rows[i] = ms[i].rows;
+        g.first[i] = tiles;
+        tiles += (ms[i].rows + NR - 1) / NR;
+    }
+    g.first[n] = tiles;
+    for (uint32_t i = n + 1; i <= static_cast<uint32_t>(kMaxGroup); ++i) g.first[i] = 0x7FFFFFFFu;
+    const uint32_t cols = ms[0].cols;
+    const uint32_t want = (tiles + kStreamWaves - 1) / kStreamWaves;
+    const uint32_t cap = tune_knob("QMV_STREAM_WG", 256);
+    const uint32_t blocks = want < cap ? want : cap;
+    // QMV_STREAM_ORDER=1: contiguous tile ranges per workgroup
+    const uint32_t per_wg = tune_knob("QMV_STREAM_ORDER", 1) == 1 ? (tiles + blocks - 1) / blocks : 0;
+    const size_t lds = static_cast<size_t>(gemv_lds_bytes<WT>(cols, NB));
+    const float* xp = x + static_cast<uint64_t>(done) * cols;
+    if (tune_knob("QMV_STREAM_DEPTH", 2) == 3)
+        hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 3>), dim3(blocks),
+                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg);
+    else
+        hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 2>), dim3(blocks),
+                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg);
+    return hipGetLastError();
+}
+
+// Rows per tile of the streaming kernel: 4, 2, 1 for 1, 2, 3..4 steps per
+// row (two tiles of quants in flight stay at <= 8 loads per lane); 0 when
+// the rows need more steps.
+template <uint32_t WT>
+uint32_t stream_rows(uint32_t cols) {
+    const uint32_t S = (cols / DigitLayout<WT>::CW + 63) / 64;
+    return S == 1 ? 4 : S == 2 ? 2 : S <= 4 ? 1 : 0;
+}
+
+// Streaming pays for rows of two steps (a Q4_0 row of 4096 weights, say)
+// once the tiles outnumber the resident waves (4096) by a margin; with one
+// step per row the one-shot kernel's many small workgroups read faster.
+// QMV_STREAM_MIN overrides the threshold.
+template <uint32_t WT>
+bool use_stream(const MatView* ms, uint32_t n) {
+    const uint32_t nr = stream_rows<WT>(ms[0].cols);
+    if (nr != 2) return false;
+    uint64_t tiles = 0;
+    for (uint32_t i = 0; i < n; ++i) tiles += (ms[i].rows + nr - 1) / nr;
+    return tiles >= tune_knob("QMV_STREAM_MIN", 6144);
+}
+
+// One streaming launch for a single activation vector (the decode case).
+template <uint32_t WT, bool SF16>
+hipError_t stream_pass(const MatView* ms, uint32_t n, const float* x, float* const* ys,
+                       hipStream_t s) {
+    switch (stream_rows<WT>(ms[0].cols)) {
+        case 4: return stream_launch<WT, SF16, 4, 1, 1>(ms, n, x, ys, 0, s);
+        case 2: return stream_launch<WT, SF16, 2, 1, 2>(ms, n, x, ys, 0, s);
+        default: return stream_launch<WT, SF16, 1, 1, 4>(ms, n, x, ys, 0, s);
+    }
 }
 
 // Launch shape: S = steps per row (64 chunks each).  Rows per wave NR: up to
 // 4 for S = 1 and 2 for S = 2 (a wave's quant loads stay <= 4 per lane), 1
 // beyond, and never so many that fewer than 2048 waves (8 per compute unit)
-// remain.  Eight waves per workgroup share one LDS copy of the activations.
-// QMV_GEMV_NR / QMV_GEMV_WAVES override (tuning sweeps).
+// remain.  Eight waves per workgroup share one LDS copy of the activations,
+// sixteen for rows of more than four steps (fewer copies of a wide vector).
+// QMV_GEMV_NR overrides NR (tuning sweeps).
 template <uint32_t WT, bool SF16, int NB>
 hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) {
-    constexpr uint32_t CW = (WT == kQ4) ? 32 : 16;
+    constexpr uint32_t CW = DigitLayout<WT>::CW;
     const uint32_t S = (m.cols / CW + 63) / 64;
-    const uint64_t lds = gemv_lds_bytes<WT>(m.cols, NB);
-    const uint64_t row_bytes = (WT == kQ4) ? m.cols / 2 : m.cols;
-    if (lds <= 64 * 1024 && S <= 16 && 4 * row_bytes < 0xFFFFFFF0ull) {
-        uint32_t nr = S == 1 ? 4 : S == 2 ? 2 : 1;
-        while (nr > 1 && m.rows / nr < 2048) nr /= 2;
-        nr = tune_knob("QMV_GEMV_NR", nr);
-        const uint32_t waves = tune_knob("QMV_GEMV_WAVES", 8);
-        const size_t l = static_cast<size_t>(lds);
-#define QMV_ONESHOT(NR_, SMAX_)                                                          \
-    if (nr == NR_ && S <= SMAX_)                                                         \
-        return waves == 8 ? gemv_oneshot_launch<WT, SF16, NR_, NB, SMAX_, 8>(m, x, y, l, s) \
-                          : gemv_oneshot_launch<WT, SF16, NR_, NB, SMAX_, 4>(m, x, y, l, s);
-        QMV_ONESHOT(4, 1)
-        QMV_ONESHOT(2, 1)
-        QMV_ONESHOT(2, 2)
-        QMV_ONESHOT(1, 1)
-        QMV_ONESHOT(1, 2)
-        QMV_ONESHOT(1, 4)
-        QMV_ONESHOT(1, 8)
-        QMV_ONESHOT(1, 16)
+    uint32_t nr = S == 1 ? 4 : S == 2 ? 2 : 1;
+    while (nr > 1 && m.rows / nr < 2048) nr /= 2;
+    nr = tune_knob("QMV_GEMV_NR", nr);
+    if (oneshot_fits<WT>(m.cols, NB, nr)) {
+        const size_t l = static_cast<size_t>(gemv_lds_bytes<WT>(m.cols, NB));
+#define QMV_ONESHOT(NR_, SMAX_, W_) \
+    if (nr == NR_ && S <= SMAX_) return gemv_oneshot_launch<WT, SF16, NR_, NB, SMAX_, W_>(m, x, y, l, s);
+        QMV_ONESHOT(4, 1, 8)
+        QMV_ONESHOT(2, 1, 8)
+        QMV_ONESHOT(2, 2, 8)
+        QMV_ONESHOT(1, 1, 8)
+        QMV_ONESHOT(1, 2, 8)
+        QMV_ONESHOT(1, 4, 8)
+        QMV_ONESHOT(1, 8, 16)
+        QMV_ONESHOT(1, 12, 16)
+        QMV_ONESHOT(1, 16, 16)
 #undef QMV_ONESHOT
     }
     constexpr uint32_t kWavesWanted = 256 * 8;
@@ -539,26 +1021,37 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
 template <uint32_t WT, bool SF16>
 hipError_t gemv_batched(const MatView& m, const float* x, float* y,
                         uint32_t batch, hipStream_t s) {
+    if (batch == 1 && use_stream<WT>(&m, 1)) return stream_pass<WT, SF16>(&m, 1, x, &y, s);
     uint32_t done = 0;
     while (done < batch) {
-        const uint32_t left = batch - done;
         const float* xp = x + static_cast<uint64_t>(done) * m.cols;
         float* yp = y + static_cast<uint64_t>(done) * m.rows;
+        const uint32_t nb = pass_vectors<WT>(m.cols, batch - done);
         hipError_t e;
-        uint32_t nb;
-        if (left >= 8) { nb = 8; e = gemv_pass<WT, SF16, 8>(m, xp, yp, s); }
-        else if (left >= 4) { nb = 4; e = gemv_pass<WT, SF16, 4>(m, xp, yp, s); }
-        else if (left >= 2) { nb = 2; e = gemv_pass<WT, SF16, 2>(m, xp, yp, s); }
-        else { nb = 1; e = gemv_pass<WT, SF16, 1>(m, xp, yp, s); }
+        if (nb == 8) e = gemv_pass<WT, SF16, 8>(m, xp, yp, s);
+        else if (nb == 4) e = gemv_pass<WT, SF16, 4>(m, xp, yp, s);
+        else if (nb == 2) e = gemv_pass<WT, SF16, 2>(m, xp, yp, s);
+        else e = gemv_pass<WT, SF16, 1>(m, xp, yp, s);
         if (e != hipSuccess) return e;
         done += nb;
     }
     return hipSuccess;
 }
 
+template <int NR, int NB, int SMAX4>
+hipError_t group_launch(const GroupArgs& g, uint32_t blocks, size_t lds, const float* xp,
+                        uint32_t cols, hipStream_t s) {
+    constexpr int WAVES = 8;
+    hipLaunchKernelGGL((gemv_group_kernel<NR, NB, SMAX4, WAVES>), dim3(blocks), dim3(WAVES * 64),
+                       lds, s, g, xp, cols);
+    return hipGetLastError();
+}
+
+// Rows per wave of a grouped launch: 1 (measured faster than 2 for a mixed
+// wq | wk | wv group); QMV_GROUP_NR = 2 selects two when cols <= 4096.
 template <int NB>
 hipError_t group_pass(const MatView* ms, uint32_t n, const float* x, float* const* ys,
-                      uint32_t done, hipStream_t s) {
+                      uint32_t done, uint32_t nr, hipStream_t s) {
     constexpr int WAVES = 8;
     const uint32_t cols = ms[0].cols;
     const uint32_t S4 = (cols / 32 + 63) / 64;
@@ -573,18 +1066,18 @@ hipError_t group_pass(const MatView* ms, uint32_t n, const float* x, float* cons
         g.rows[i] = ms[i].rows;
         g.kind[i] = 2 * (ms[i].wtype == kQ8) + ms[i].scale_f16;
         g.first[i] = blocks;
-        blocks += (ms[i].rows + WAVES - 1) / WAVES;
+        blocks += (ms[i].rows + WAVES * nr - 1) / (WAVES * nr);
         const uint64_t b = ms[i].wtype == kQ4 ? gemv_lds_bytes<kQ4>(cols, NB) : gemv_lds_bytes<kQ8>(cols, NB);
         lds = b > lds ? b : lds;
     }
     g.first[n] = blocks;
     const float* xp = x + static_cast<uint64_t>(done) * cols;
     const size_t l = static_cast<size_t>(lds);
-    if (S4 <= 1) hipLaunchKernelGGL((gemv_group_kernel<NB, 1, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
-    else if (S4 <= 2) hipLaunchKernelGGL((gemv_group_kernel<NB, 2, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
-    else if (S4 <= 4) hipLaunchKernelGGL((gemv_group_kernel<NB, 4, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
-    else hipLaunchKernelGGL((gemv_group_kernel<NB, 8, WAVES>), dim3(blocks), dim3(WAVES * 64), l, s, g, xp, cols);
-    return hipGetLastError();
+    if (nr == 2 && S4 <= 2) return group_launch<2, NB, 2>(g, blocks, l, xp, cols, s);
+    if (S4 <= 1) return group_launch<1, NB, 1>(g, blocks, l, xp, cols, s);
+    if (S4 <= 2) return group_launch<1, NB, 2>(g, blocks, l, xp, cols, s);
+    if (S4 <= 4) return group_launch<1, NB, 4>(g, blocks, l, xp, cols, s);
+    return group_launch<1, NB, 8>(g, blocks, l, xp, cols, s);
 }
 
 }  // namespace
@@ -597,11 +1090,18 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
                              uint32_t batch, hipStream_t s) {
     const uint32_t cols = ms[0].cols;
     const uint32_t S4 = (cols / 32 + 63) / 64;
-    bool fits = n <= static_cast<uint32_t>(kMaxGroup) && batch <= kGemvMaxBatch && S4 <= 8;
-    for (uint32_t i = 0; fits && i < n; ++i) {
-        const uint64_t row_bytes = ms[i].wtype == kQ4 ? cols / 2 : cols;
-        const uint64_t lds = ms[i].wtype == kQ4 ? gemv_lds_bytes<kQ4>(cols, 1) : gemv_lds_bytes<kQ8>(cols, 1);
-        fits = lds * (batch > 4 ? 8 : batch > 2 ? 4 : batch) <= 64 * 1024 && row_bytes < 0xFFFFFFF0ull;
+    const bool fits = n <= static_cast<uint32_t>(kMaxGroup) && batch <= kGemvMaxBatch && S4 <= 8 &&
+                      oneshot_fits<kQ4>(cols, 1, 2) && oneshot_fits<kQ8>(cols, 1, 2);
+    bool same = true;
+    for (uint32_t i = 1; i < n; ++i)
+        same = same && ms[i].wtype == ms[0].wtype && ms[i].scale_f16 == ms[0].scale_f16;
+    if (n <= static_cast<uint32_t>(kMaxGroup) && batch == 1 && same) {
+        if (ms[0].wtype == kQ4 && use_stream<kQ4>(ms, n))
+            return ms[0].scale_f16 ? stream_pass<kQ4, true>(ms, n, x, ys, s)
+                                   : stream_pass<kQ4, false>(ms, n, x, ys, s);
+        if (ms[0].wtype == kQ8 && use_stream<kQ8>(ms, n))
+            return ms[0].scale_f16 ? stream_pass<kQ8, true>(ms, n, x, ys, s)
+                                   : stream_pass<kQ8, false>(ms, n, x, ys, s);
     }
     if (!fits) {  // one launch per matrix
         for (uint32_t i = 0; i < n; ++i) {
@@ -610,15 +1110,16 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
         }
         return hipSuccess;
     }
+    const uint32_t nr_want = tune_knob("QMV_GROUP_NR", 1);
+    const uint32_t nr = (S4 <= 2 && nr_want == 2) ? 2 : 1;  // the NR = 2 kernel has SMAX4 = 2
     uint32_t done = 0;
     while (done < batch) {
-        const uint32_t left = batch - done;
+        const uint32_t nb = pass_vectors<kQ4>(cols, batch - done);
         hipError_t e;
-        uint32_t nb;
-        if (left >= 8) { nb = 8; e = group_pass<8>(ms, n, x, ys, done, s); }
-        else if (left >= 4) { nb = 4; e = group_pass<4>(ms, n, x, ys, done, s); }
-        else if (left >= 2) { nb = 2; e = group_pass<2>(ms, n, x, ys, done, s); }
-        else { nb = 1; e = group_pass<1>(ms, n, x, ys, done, s); }
+        if (nb == 8) e = group_pass<8>(ms, n, x, ys, done, nr, s);
+        else if (nb == 4) e = group_pass<4>(ms, n, x, ys, done, nr, s);
+        else if (nb == 2) e = group_pass<2>(ms, n, x, ys, done, nr, s);
+        else e = group_pass<1>(ms, n, x, ys, done, nr, s);
         if (e != hipSuccess) return e;
         done += nb;
     }
