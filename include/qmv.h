@@ -123,11 +123,21 @@ int qmv_destroy(qmv_handle h);
  * Decode product (GEMV), y[t][r] = sum_c W[r][c] * x[t][c], for t < batch.
  * x: float32 [batch][cols], y: float32 [batch][rows], row-major, device
  * memory.  The weights stay quantized in device memory and are decoded in
- * registers; accumulation is float32.  Each output is within
- * 2e-3 * sum_c |W[r][c]| |x[t][c]| of the exact product.  Small batches run
- * a bandwidth-bound vector kernel; large batches (an LM head over a prefill
- * batch, say) run the matrix-core kernel with each float32 activation split
- * into two bfloat16 terms.
+ * registers.
+ * Batches up to 8 run the bandwidth-bound vector kernels: every activation is
+ * represented, per block of 32 (the span of one weight scale), in 24-bit
+ * fixed point relative to the block's largest magnitude amax (an error of at
+ * most 2^-22 * amax), the block sums of weight codes times activation digits
+ * are exact integer dot products (the Q8_0 activation quantization of the
+ * .mlb page's "Quantization rule", with three int8 digits instead of one),
+ * and blocks are accumulated in float32.  An output is then within
+ * 2^-22 * sum_b amax_b * sum_{c in b} |W[r][c]| of the exact product, plus
+ * float32 rounding; this is within 2e-3 * sum_c |W[r][c]| |x[t][c]| unless,
+ * inside blocks, the nonzero weights meet only activations below about
+ * amax / 8000.  A non-finite activation makes the outputs of its batch row
+ * NaN.  Larger batches (an LM head over a prefill batch, say) run the
+ * matrix-core kernel with each float32 activation split into two bfloat16
+ * terms; each output is then within 2e-3 * sum_c |W[r][c]| |x[t][c]|.
  * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no upload),
  * QMV_E_DEVICE (launch failure).
  */
@@ -141,8 +151,8 @@ int qmv_gemv(qmv_handle h, const float *x, float *y, uint32_t batch,
  * w1, w3 — the .mlb page's body order), and it saves the fixed start-up and
  * drain of every launch after the first.  hs: n handles (any mix of Q4_0 /
  * Q8_0 and scale types); x: float32 [batch][cols]; ys: a host array of n
- * device pointers, float32 [batch][rows_i].  Each output is what qmv_gemv
- * would compute for that matrix, within the same bound.
+ * device pointers, float32 [batch][rows_i].  Each output is bit for bit
+ * what qmv_gemv computes for that matrix (the same per-row arithmetic).
  * Errors: QMV_E_ARG (n not in 1..8, null or misaligned pointer, batch 0, a
  * handle not uploaded), QMV_E_SHAPE (cols differ), QMV_E_DEVICE.
  */
