@@ -1128,7 +1128,11 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
 
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
                        uint32_t batch, hipStream_t s) {
-    if (batch > kGemvMaxBatch) return launch_gemm(m, x, true, y, batch, nullptr, s);
+    if (batch > kGemvMaxBatch) {
+        const hipError_t e = launch_gemv_mfma(m, x, y, batch, s);
+        if (e != hipErrorNotSupported) return e;
+        return launch_gemm(m, x, true, y, batch, nullptr, s);
+    }
     if (m.wtype == kQ4) {
         return m.scale_f16 ? gemv_batched<kQ4, true>(m, x, y, batch, s)
                            : gemv_batched<kQ4, false>(m, x, y, batch, s);

@@ -11,6 +11,7 @@ struct MatView {
     const uint8_t* q;
     const void* d;
     uint32_t wtype, scale_f16, rows, cols;
+    int32_t dexp;  // max |d| in [2^(dexp-1), 2^dexp); 0 if all zero or non-finite
 };
 
 // y[t][r] = sum_c W[r][c] x[t][c]; x f32 [batch][cols], y f32 [batch][rows].
@@ -29,6 +30,12 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
 size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
                        uint32_t batch, float* workspace, hipStream_t stream);
+
+// Batched product on the matrix cores with f16 operands (Q8_0 with f16
+// scales, cols a multiple of 256 up to 1024, any batch): returns
+// hipErrorNotSupported for other matrices, which then take launch_gemm.
+hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
+                            hipStream_t stream);
 
 // out[i][c] = fl32(v * d) of row ids[i] (zeros for an id out of range).
 hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,

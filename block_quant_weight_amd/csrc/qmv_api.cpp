@@ -16,6 +16,7 @@ struct qmv_mat {
     qmv::Layout layout;
     uint8_t* dev = nullptr;  // q at dev, d at dev + d_offset (hipMalloc'd)
     int device = -1;
+    int32_t dexp = 0;        // exponent of the largest scale magnitude
 };
 
 namespace {
@@ -88,7 +89,7 @@ int workspace_for(hipStream_t stream, size_t bytes, void** out) {
 qmv::MatView view(const qmv_mat* h) {
     const qmv::Layout& L = h->layout;
     return qmv::MatView{h->dev, h->dev + L.d_offset, L.wtype, L.scale_f16,
-                        L.rows, L.cols};
+                        L.rows, L.cols, h->dexp};
 }
 
 }  // namespace
@@ -134,6 +135,7 @@ int qmv_upload(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
     }
     h->dev = d;
     h->device = dev;
+    h->dexp = qmv::scale_exponent(L, src);
     return QMV_OK;
 }
 

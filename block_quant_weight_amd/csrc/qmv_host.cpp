@@ -8,6 +8,7 @@
 // q8_mask paragraph, and "Validation done by the loader" (error classes,
 // overflow-checked size arithmetic).
 #include <cstddef>
+#include <cmath>
 #include <cstdint>
 
 #include "qmv.h"
@@ -81,6 +82,40 @@ int check_bytes(const Layout& L, const void* src, uint64_t nbytes) {
             if (p[i] == 0x80) return QMV_E_FORMAT;
     }
     return QMV_OK;
+}
+
+int32_t scale_exponent(const Layout& L, const void* src) {
+    const uint8_t* d = static_cast<const uint8_t*>(src) + L.d_offset;
+    const uint64_t n = L.d_bytes / (L.scale_f16 ? 2 : 4);
+    float amax = 0.f;
+    if (L.scale_f16) {
+        // magnitudes of IEEE binary16 values order like their low 15 bits
+        uint16_t m = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint16_t b;
+            __builtin_memcpy(&b, d + 2 * i, 2);
+            b &= 0x7FFF;
+            m = b > m ? b : m;
+        }
+        if (m >= 0x7C00) return 0;  // inf or NaN
+        const int e = m >> 10, f = m & 0x3FF;
+        amax = e == 0 ? std::ldexp(static_cast<float>(f), -24)
+                      : std::ldexp(static_cast<float>(1024 + f), e - 25);
+    } else {
+        uint32_t m = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            uint32_t b;
+            __builtin_memcpy(&b, d + 4 * i, 4);
+            b &= 0x7FFFFFFFu;
+            m = b > m ? b : m;
+        }
+        if (m >= 0x7F800000u) return 0;
+        __builtin_memcpy(&amax, &m, 4);
+    }
+    if (amax == 0.f) return 0;
+    int e = 0;
+    (void)std::frexp(amax, &e);
+    return e;
 }
 
 }  // namespace qmv

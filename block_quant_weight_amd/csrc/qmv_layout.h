@@ -20,4 +20,10 @@ int compute_layout(uint32_t wtype, uint32_t scale_f16, uint32_t rows,
 // Q8_0 quant equal to -128.  QMV_OK, QMV_E_ARG or QMV_E_FORMAT.
 int check_bytes(const Layout& L, const void* src, uint64_t nbytes);
 
+// Binary exponent E of the largest scale magnitude of a checked buffer
+// (max |d| in [2^(E-1), 2^E)); 0 when every scale is zero or some scale is
+// inf or NaN.  Kernels that hold weights in a narrow float type scale them
+// by 2^-E so that no product overflows.
+int32_t scale_exponent(const Layout& L, const void* src);
+
 }  // namespace qmv

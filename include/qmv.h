@@ -135,9 +135,17 @@ int qmv_destroy(qmv_handle h);
  * float32 rounding; this is within 2e-3 * sum_c |W[r][c]| |x[t][c]| unless,
  * inside blocks, the nonzero weights meet only activations below about
  * amax / 8000.  A non-finite activation makes the outputs of its batch row
- * NaN.  Larger batches (an LM head over a prefill batch, say) run the
- * matrix-core kernel with each float32 activation split into two bfloat16
- * terms; each output is then within 2e-3 * sum_c |W[r][c]| |x[t][c]|.
+ * NaN.  Larger batches (an LM head over a batch of hidden states, say) run
+ * on the matrix cores: for a Q8_0 matrix with f16 scales and cols a multiple
+ * of 256 up to 1024, in f16 — each token's activations scaled by a power of
+ * two and rounded to f16, each weight fl16(q * d * 2^k) with one k for the
+ * matrix (from its largest scale, found at upload) — with float32
+ * accumulation, within about 2^-10 * sum_c |W[r][c]| |x[t][c]| for
+ * activations within 2^28 of their token's largest and scales within 2^22
+ * of the matrix's largest; otherwise with weights rounded to bfloat16 and
+ * each float32 activation split into two bfloat16 terms, within
+ * 2e-3 * sum_c |W[r][c]| |x[t][c]|.  A non-finite activation makes its
+ * token's outputs NaN on the f16 path.
  * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no upload),
  * QMV_E_DEVICE (launch failure).
  */

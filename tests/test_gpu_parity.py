@@ -369,3 +369,44 @@ def test_gemv_nonfinite_activation_gives_nan():
         assert np.all(np.isfinite(y[2]))
     finally:
         Q.qmv_destroy(h)
+
+
+# ---- batched GEMV on the f16 matrix-core path (Q8_0, f16 scales, cols % 256) --
+
+@pytest.mark.parametrize("R,C", [(1, 256), (31, 512), (300, 1024), (1000, 768)])
+@pytest.mark.parametrize("batch", [9, 33, 64, 65, 130])
+def test_gemv_batched_f16_matrix_core_path(R, C, batch):
+    img = K.make_image(300 + R, batch, K.Q8, 1, R, C, lo=-1e-2)   # negative scales too
+    h = K.upload(img, K.Q8, 1, R, C)
+    try:
+        x = K.make_x(300 + R, C + batch, batch, C)
+        ref, norm = O.product(img, K.Q8, 1, R, C, x, threads=K.THREADS)
+        close(K.gpu_gemv(h, x), ref, norm, f"gemv-f16 {R}x{C} b{batch}")
+    finally:
+        Q.qmv_destroy(h)
+
+
+def test_gemv_batched_f16_path_ranges_and_nonfinite():
+    # scales up to 1000 (q * d up to 127000, past f16's 65504: the weights are
+    # scaled by 2^-k to stay in f16), token rows whose magnitudes differ by
+    # 2^40 from token to token and by 2^12 inside a token, and NaN / inf in
+    # two tokens
+    R, C, B = 200, 512, 20
+    img = K.make_image(310, 0, K.Q8, 1, R, C, lo=1.0, hi=1000.0)
+    h = K.upload(img, K.Q8, 1, R, C)
+    try:
+        g = np.random.default_rng(310)
+        x = K.make_x(310, 1, B, C).astype(np.float64)
+        x *= np.exp2(g.uniform(-20, 20, size=(B, 1)))       # per-token magnitude
+        x *= np.exp2(g.uniform(-12, 0, size=(B, C)))        # spread inside a token
+        x = x.astype(np.float32)
+        ref, norm = O.product(img, K.Q8, 1, R, C, x, threads=K.THREADS)
+        close(K.gpu_gemv(h, x), ref, norm, "gemv-f16 ranges")
+        x[3, 17] = np.nan
+        x[11, 400] = -np.inf
+        y = K.gpu_gemv(h, x)
+        assert np.all(np.isnan(y[3])) and np.all(np.isnan(y[11]))
+        keep = [t for t in range(B) if t not in (3, 11)]
+        assert np.all(np.isfinite(y[keep]))
+    finally:
+        Q.qmv_destroy(h)
