@@ -85,15 +85,15 @@ LAYER_GROUPS = [(0, 1, 2), (3,), (4, 5), (6,)]
 # The kernel that the library's dispatch runs for each workload's largest
 # launch (the roofline's kernel), and the source file it is built from.
 DOMINANT_KERNEL = {
-    "q4_gemv_4096": ("gemv_oneshot_kernel", "gemv"),
-    "q8_gemv_512": ("gemv_oneshot_kernel", "gemv"),
-    "decode_layer": ("gemv_stream_kernel (w1|w3)", "gemv"),
-    "decode_layer_7": ("gemv_oneshot_kernel (w2)", "gemv"),
-    "lm_head_b1": ("gemv_oneshot_kernel", "gemv"),
-    "lm_head_b64": ("gemm_kernel (f32 activations as two bf16 terms)", "gemm"),
-    "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm"),
-    "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm"),
-    "embed_64": ("embed_kernel", "embed"),
+    "q4_gemv_4096": ("gemv_oneshot_kernel", "gemv.hip"),
+    "q8_gemv_512": ("gemv_oneshot_kernel", "gemv.hip"),
+    "decode_layer": ("gemv_stream_kernel (w1|w3)", "gemv.hip"),
+    "decode_layer_7": ("gemv_oneshot_kernel (w2)", "gemv.hip"),
+    "lm_head_b1": ("gemv_oneshot_kernel", "gemv.hip"),
+    "lm_head_b64": ("gemv_mfma_kernel (f16 operands)", "gemv_mfma.hip"),
+    "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm.hip"),
+    "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
+    "embed_64": ("embed_kernel", "misc.hip"),
 }
 
 
@@ -147,15 +147,13 @@ def make_image(config, m, wt, sf, r, c):
     return img
 
 
-def kernel_source_hash(kind):
-    f = {"gemv": "gemv.hip", "gemm": "gemm.hip", "embed": "misc.hip"}.get(kind)
-    if f is None:
-        return None
-    with open(os.path.join(ROOT, "block_quant_weight_amd", "csrc", f), "rb") as fh:
+def kernel_source_hash(src):
+    """sha256[:16] of a kernel source file under block_quant_weight_amd/csrc."""
+    with open(os.path.join(ROOT, "block_quant_weight_amd", "csrc", src), "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(name, kind):
+def traffic_from_profiles(name, src):
     """HBM bytes per launch of the roofline's kernel from the committed
     counter summary, if it was taken on the kernel source as it stands."""
     path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
@@ -164,7 +162,7 @@ def traffic_from_profiles(name, kind):
     try:
         with open(path) as fh:
             t = json.load(fh)
-        if t.get("kernel_source_sha256_16") != kernel_source_hash(kind):
+        if t.get("kernel_source_sha256_16") != kernel_source_hash(src):
             return None
         return t.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -419,7 +417,7 @@ def main():
         dom_desc = {"algorithmic_bytes_per_launch": step_bytes if kind != "gemm" else None,
                     "flops_per_launch": step_flops if kind == "gemm" else None,
                     "us_per_launch": round(ms_step * 1e3, 3)}
-    kname, ksrc = DOMINANT_KERNEL.get(args.workload, ("?", kind))
+    kname, ksrc = DOMINANT_KERNEL[args.workload]
     traffic = traffic_from_profiles(args.workload, ksrc)
     roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
             "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -1,5 +1,5 @@
 // Batched decode product on the matrix cores, f16 operands: Y[t][r] =
-// sum_c W[r][c] x[t][c] for a Q8_0 matrix with f16 scales and up to 1024
+// sum_c W[r][c] x[t][c] for a Q8_0 matrix with f16 scales and 512 or 1024
 // columns over batches above 8 — the shared classifier (LM head) applied to a
 // batch of hidden states (Krafla ".mlb model, version 1" page, header field
 // `shared_classifier`; "Body" for the product, "Q8_0" for w = q * d).
@@ -24,13 +24,19 @@
 // wave walks tiles of 32 weight rows; tokens are the A operand (two 32-token
 // tiles) and weight rows the B operand of v_mfma_f32_32x32x16_f16, so a
 // lane's output column is a weight row and stores of 32 consecutive rows per
-// token coalesce.  Lane (r, h) = (lane % 32, lane / 32) loads 16 quant bytes
-// of row r at 32j + 16h per block j (one 16-byte load per lane and block, the
-// two halves of a lane pair covering the 32-byte block), which feed two
-// matrix-core steps; the activations are read with the same split of k, so
-// A and B agree on which k each step sums.  The loads run kRing blocks ahead
-// through a ring of registers (raw buffer loads: past the last tile they get
-// an out-of-range offset and return zeros, so the ring needs no branches).
+// token coalesce.  The B operand wants lane (r, h) = (lane % 32, lane / 32)
+// to hold 8 + 8 quants of row r (block j, half h); loading that directly
+// makes every load instruction touch 32 rows, which the address and L1 units
+// serve one lane at a time.  Instead a wave loads a pair of blocks of its 32
+// rows with two instructions of 16 rows x 64 contiguous bytes, writes them to
+// its own 2 KiB LDS slice (16-byte chunks XOR-swizzled by row so that both
+// the writes and the reads below are free of bank conflicts) and reads them
+// back in the operand layout.  The activations are read with the same split
+// of k, so A and B agree on which k each step sums.  Loads go by groups of 8
+// blocks (4 pairs of quant loads and one 16-byte load of a row's 8 scales) in
+// two register sets, the next group in flight while one is multiplied,
+// across tile boundaries; raw buffer loads past the wave's last group get an
+// out-of-range offset and return zeros, so the loads need no branches.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -44,8 +50,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kTokens = 64;     // tokens per pass (two 32-token tiles)
 constexpr int kMaxCols = 1024;  // activations of one pass must fit LDS
-constexpr int kRing = 8;        // blocks of quants in flight per wave
 constexpr uint32_t kOob = 0xFFFFFFF0u;
+constexpr int kXBytes = kTokens * (2 * kMaxCols + 16);
+constexpr int kSlice = 32 * 64;  // a wave's LDS slice: 32 rows x one block pair
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -87,145 +94,206 @@ __device__ __forceinline__ void dequant16(const u32x4 w, f16x2 dd, f16x8 (&out)[
         }
 }
 
+// Byte offset in a wave's slice of row n's 16-byte chunk c (0..3) of a block
+// pair: chunk index XORed with bits 1..2 of the row, so that 8 consecutive
+// lanes of either access pattern hit 8 different groups of four banks.
+__device__ __forceinline__ uint32_t slice_off(uint32_t n, uint32_t c) {
+    return n * 64 + ((c ^ ((n >> 1) & 3)) << 4);
+}
+
+// Loads of one group of 8 blocks (4 block pairs) of a tile: the quants, as
+// two 16-row x 64-byte loads per pair, and this lane's row's 8 scales.
+struct Group {
+    u32x4 q[4][2];
+    u32x4 sc;
+};
+
+template <int NJ>
 __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
     const uint8_t* __restrict__ q, const uint16_t* __restrict__ d, const float* __restrict__ x,
-    float* __restrict__ y, uint32_t rows, uint32_t cols, uint32_t ntok, float wscale,
-    float inv_wscale) {
-    __shared__ __align__(16) uint8_t xs[kTokens * (2 * kMaxCols + 16)];
+    float* __restrict__ y, uint32_t rows, uint32_t ntok, float wscale, float inv_wscale) {
+    constexpr uint32_t cols = 32 * NJ;
+    constexpr uint32_t NG = NJ / 8;   // groups of 8 blocks per row
+    static_assert(NG % 2 == 0, "groups alternate between two register sets within a tile");
+    __shared__ __align__(16) uint8_t xs[kXBytes];
+    __shared__ __align__(16) uint8_t wsl[kWaves * kSlice];
     __shared__ float tinv[kTokens];
     const int tid = threadIdx.x, lane = tid & 63;
     const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t P = 2 * cols + 16;  // LDS bytes per token
-    const uint32_t nj = cols / 32;     // blocks per row = steps per tile
+    constexpr uint32_t P = 2 * cols + 16;  // LDS bytes per token
     const uint32_t r = lane & 31, h = lane >> 5;
+    uint8_t* slice = wsl + wid * kSlice;
 
-    // ---- ring prologue: the first kRing blocks of this wave's tiles ----
     const uint32_t tiles = (rows + 31) / 32;
     const uint32_t first = blockIdx.x * kWaves + wid;
     const uint32_t stride = gridDim.x * kWaves;
     const uint32_t my_tiles = first < tiles ? (tiles - first + stride - 1) / stride : 0;
-    const uint32_t nsteps = my_tiles * nj;
-    const __amdgpu_buffer_rsrc_t qrs = rsrc(q, rows * cols);
-    const __amdgpu_buffer_rsrc_t drs = rsrc(d, rows * nj * 2);
-    u32x4 rq[kRing];
-    uint32_t rd[kRing];
-    uint32_t lt = 0, lj = 0;  // tile (of this wave) and block of the next load
-    auto load = [&](int slot) {
-        const uint32_t row = (first + lt * stride) * 32 + r;
-        const bool ok = lt < my_tiles && row < rows;
-        const uint32_t qo = ok ? row * cols + 32 * lj + 16 * h : kOob;
-        const uint32_t dof = ok ? (row * nj + lj) * 2 : kOob;
-        rd[slot] = __builtin_amdgcn_raw_buffer_load_b16(drs, dof, 0, 0);
-        rq[slot] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qo, 0, 0);
-        if (++lj == nj) { lj = 0; ++lt; }
-    };
+    const uint32_t ngroups = my_tiles * NG;
+
+    // group G of this wave: tile G / NG (rows from (first + tile * stride) * 32),
+    // blocks 8 (G % NG) ...; a group past the wave's last gets out-of-range
+    // offsets
+    // (a dead group reads through empty buffer ranges: no select around the
+    // offsets, which the compiler would turn into branches around the loads)
+    // Tile t takes its groups in the order rot(t), rot(t) + 1, ... (mod NG):
+    // waves start at different column ranges, which spreads their
+    // concurrent reads over the memory channels.
+    auto rot = [&](uint32_t tile) { return (first + tile) % NG; };
+    auto load_group = [&](uint32_t G, Group& dst) {
+        const uint32_t tile = G / NG, g = (G % NG + rot(tile)) % NG;
+        const bool live = G < ngroups;
+        const uint32_t base = live ? (first + tile * stride) * 32 : 0;
+        const __amdgpu_buffer_rsrc_t gq = rsrc(q, live ? rows * cols : 0);
+        const __amdgpu_buffer_rsrc_t gd = rsrc(d, live ? rows * NJ * 2 : 0);
+        // the scales first: loads complete in order, so the group's first
+        // block then waits for its own quants only
+        dst.sc = __builtin_amdgcn_raw_buffer_load_b128(gd, (base + r) * NJ * 2 + 16 * g, 0, 0);
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) load(u);
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t row = base + 16 * k + (lane >> 2);
+                const uint32_t off = row * cols + 256 * g + 64 * p + 16 * (lane & 3);
+                dst.q[p][k] = __builtin_amdgcn_raw_buffer_load_b128(gq, off, 0, 0);
+            }
+    };
+
+    Group ga, gb;
+    load_group(0, ga);
+    load_group(1, gb);
 
     // ---- activations -> f16 in LDS: wave w converts tokens w, w + 8, ...,
     // with all of its loads requested first (one round trip, not eight) ----
     constexpr int TPW = kTokens / kWaves;  // tokens per wave
-    float4 v[TPW][4];
+    {
+        float4 v[TPW][4];
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        const uint32_t t = wid + kWaves * k;
+        for (int k = 0; k < TPW; ++k) {
+            const uint32_t t = wid + kWaves * k;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c4 = lane + 64 * i;  // float4 index within the token
-            v[k][i] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < ntok && 4 * c4 < cols)
-                v[k][i] = reinterpret_cast<const float4*>(x + static_cast<uint64_t>(t) * cols)[c4];
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        const uint32_t t = wid + kWaves * k;
-        uint32_t m = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m = max(m, __builtin_bit_cast(uint32_t, v[k][i].x) & 0x7FFFFFFFu);
-            m = max(m, __builtin_bit_cast(uint32_t, v[k][i].y) & 0x7FFFFFFFu);
-            m = max(m, __builtin_bit_cast(uint32_t, v[k][i].z) & 0x7FFFFFFFu);
-            m = max(m, __builtin_bit_cast(uint32_t, v[k][i].w) & 0x7FFFFFFFu);
-        }
-        m = wave_max_u32(m);
-        const bool finite = m < 0x7F800000u;
-        const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
-        const int sh = finite ? 14 - E : 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c4 = lane + 64 * i;
-            if (4 * c4 < cols) {
-                float4 a = v[k][i];
-                if (!finite) a = make_float4(0.f, 0.f, 0.f, 0.f);
-                const f16x2 p0 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.x, sh)),
-                                  static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.y, sh))};
-                const f16x2 p1 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.z, sh)),
-                                  static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.w, sh))};
-                *reinterpret_cast<uint2*>(xs + t * P + 8 * c4) =
-                    make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c4 = lane + 64 * i;  // float4 index within the token
+                v[k][i] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t < ntok && 4 * c4 < cols)
+                    v[k][i] = reinterpret_cast<const float4*>(x + static_cast<uint64_t>(t) * cols)[c4];
             }
         }
-        if (lane == 0)
-            tinv[t] = t >= ntok ? 0.f
-                    : finite ? __builtin_amdgcn_ldexpf(1.0f, -sh) * inv_wscale
-                             : __builtin_bit_cast(float, 0x7FC00000u);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const uint32_t t = wid + kWaves * k;
+            uint32_t m = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                m = max(m, __builtin_bit_cast(uint32_t, v[k][i].x) & 0x7FFFFFFFu);
+                m = max(m, __builtin_bit_cast(uint32_t, v[k][i].y) & 0x7FFFFFFFu);
+                m = max(m, __builtin_bit_cast(uint32_t, v[k][i].z) & 0x7FFFFFFFu);
+                m = max(m, __builtin_bit_cast(uint32_t, v[k][i].w) & 0x7FFFFFFFu);
+            }
+            m = wave_max_u32(m);
+            const bool finite = m < 0x7F800000u;
+            const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
+            const int sh = finite ? 14 - E : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c4 = lane + 64 * i;
+                if (4 * c4 < cols) {
+                    float4 a = v[k][i];
+                    if (!finite) a = make_float4(0.f, 0.f, 0.f, 0.f);
+                    const f16x2 p0 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.x, sh)),
+                                      static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.y, sh))};
+                    const f16x2 p1 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.z, sh)),
+                                      static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.w, sh))};
+                    *reinterpret_cast<uint2*>(xs + t * P + 8 * c4) =
+                        make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
+                }
+            }
+            if (lane == 0)
+                tinv[t] = t >= ntok ? 0.f
+                        : finite ? __builtin_amdgcn_ldexpf(1.0f, -sh) * inv_wscale
+                                 : __builtin_bit_cast(float, 0x7FC00000u);
+        }
     }
     __syncthreads();
 
-    // ---- tiles: kRing blocks per round; a tile's nj blocks are a whole
-    // number of rounds (cols % (32 * kRing) == 0), so tiles end between
-    // rounds.  Stores are raw buffer stores (a token or row past the end gets
-    // an out-of-range offset and is dropped, no branch).
     const __amdgpu_buffer_rsrc_t yrs = rsrc(y, ntok * rows * 4);
     f32x16 acc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mt][v] = 0.f;
-    uint32_t ct = 0, cj = 0;  // tile and first block of the round being multiplied
-    for (uint32_t s0 = 0; s0 < nsteps; s0 += kRing) {
+        for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
+
+    // multiplies group G (blocks 8g .. 8g + 7 of its tile) into acc
+    auto run_group = [&](const Group& gr, uint32_t g) {
 #pragma unroll
-        for (int u = 0; u < kRing; ++u) {
-            // weights of block cj + u: d' = d * 2^(8 - E_d), exact in f16
-            const _Float16 ds = static_cast<_Float16>(
-                static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(rd[u]))) * wscale);
-            const f16x2 dd = {ds, ds};
-            f16x8 wf[2];
-            dequant16(rq[u], dd, wf);
-            load(u);  // the ring slot is free again: the block kRing ahead
-            // activations of the same block, both token tiles, same split of k
-            f16x8 xf[2][2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint8_t* p = xs + (32 * mt + r) * P + 2 * (32 * (cj + u) + 16 * h);
-                xf[mt][0] = *reinterpret_cast<const f16x8*>(p);
-                xf[mt][1] = *reinterpret_cast<const f16x8*>(p + 16);
-            }
+        for (int p = 0; p < 4; ++p) {
+            // pair p to the slice in the loaded layout, then back per block
+            // in the operand layout
 #pragma unroll
             for (int k = 0; k < 2; ++k)
+                *reinterpret_cast<u32x4*>(slice + slice_off(16 * k + (lane >> 2), lane & 3)) = gr.q[p][k];
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[mt][k], wf[k], acc[mt], 0, 0, 0);
-        }
-        cj += kRing;
-        if (cj == nj) {
-            const uint32_t row = (first + ct * stride) * 32 + r;
-            const bool rok = row < rows;
+            for (int b = 0; b < 2; ++b) {
+                const int jj = 2 * p + b;          // block within the group
+                const uint32_t j = 8 * g + jj;     // block within the row
+                const u32x4 w = *reinterpret_cast<const u32x4*>(slice + slice_off(r, 2 * b + h));
+                const uint32_t sbits = gr.sc[jj / 2] >> (16 * (jj % 2));
+                const _Float16 ds = static_cast<_Float16>(
+                    static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(sbits))) * wscale);
+                const f16x2 dd = {ds, ds};
+                f16x8 wf[2];
+                dequant16(w, dd, wf);
+                f16x8 xf[2][2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const uint32_t t = 32 * mt + 8 * (v / 4) + 4 * h + (v % 4);
-                    const uint32_t off = (rok && t < ntok) ? (t * rows + row) * 4 : kOob;
-                    // the store takes the 32-bit pattern (an unsigned int)
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(uint32_t, acc[mt][v] * tinv[t]), yrs, off, 0, 0);
-                    acc[mt][v] = 0.f;
+                for (int mt = 0; mt < 2; ++mt) {
+                    const uint8_t* xp = xs + (32 * mt + r) * P + 2 * (32 * j + 16 * h);
+                    xf[mt][0] = *reinterpret_cast<const f16x8*>(xp);
+                    xf[mt][1] = *reinterpret_cast<const f16x8*>(xp + 16);
                 }
-            cj = 0;
-            ++ct;
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xf[mt][k], wf[k], acc[mt], 0, 0, 0);
+            }
         }
+    };
+    // stores tile `tile` (raw buffer stores: a token or row past the end gets
+    // an out-of-range offset and is dropped) and clears acc
+    auto store_tile = [&](uint32_t tile) {
+        const uint32_t row = (first + tile * stride) * 32 + r;
+        const bool rok = row < rows;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t t = 32 * mt + 8 * (e / 4) + 4 * h + (e % 4);
+                const uint32_t off = (rok && t < ntok) ? (t * rows + row) * 4 : kOob;
+                // the store takes the 32-bit pattern (an unsigned int)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[mt][e] * tinv[t]),
+                                                      yrs, off, 0, 0);
+                acc[mt][e] = 0.f;
+            }
+    };
+
+    // tiles of NG groups (NG even): group g of a tile runs from register set
+    // g % 2, which is then refilled with the group two ahead (the next tile's
+    // first groups at the end), so the sequence is static and the tile's
+    // outputs are stored after its last group
+    for (uint32_t tile = 0; tile < my_tiles; ++tile) {
+        // (scheduling barriers keep each group's work in place: letting the
+        // scheduler interleave whole groups runs out of registers)
+#pragma unroll
+        for (uint32_t g = 0; g < NG; g += 2) {
+            run_group(ga, (g + rot(tile)) % NG);
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(tile * NG + g + 2, ga);
+            __builtin_amdgcn_sched_barrier(0);
+            run_group(gb, (g + 1 + rot(tile)) % NG);
+            __builtin_amdgcn_sched_barrier(0);
+            load_group(tile * NG + g + 3, gb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        store_tile(tile);
     }
 }
 
@@ -233,10 +301,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
 
 hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
                             hipStream_t s) {
-    // Q8_0 with f16 scales, cols a multiple of 256 fitting one pass of
-    // activations in LDS, and weights and outputs within 32-bit buffer offsets
-    if (m.wtype != kQ8 || !m.scale_f16 || m.cols > static_cast<uint32_t>(kMaxCols) ||
-        m.cols % (32 * kRing) != 0 || static_cast<uint64_t>(m.rows) * m.cols >= 0xFFFFFFF0ull ||
+    // Q8_0 with f16 scales, cols 512 or 1024 (an even number of groups of 8
+    // blocks, activations of one pass in LDS), and weights and outputs within
+    // 32-bit buffer offsets
+    if (m.wtype != kQ8 || !m.scale_f16 || (m.cols != 512 && m.cols != 1024) ||
+        static_cast<uint64_t>(m.rows) * m.cols >= 0xFFFFFFF0ull ||
         static_cast<uint64_t>(m.rows) * kTokens * 4 >= 0xFFFFFFF0ull)
         return hipErrorNotSupported;
     const float wscale = ldexpf(1.0f, 8 - m.dexp);
@@ -246,9 +315,14 @@ hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t
     const uint32_t blocks = want < 256 ? want : 256;
     for (uint32_t done = 0; done < batch; done += kTokens) {
         const uint32_t nt = batch - done < static_cast<uint32_t>(kTokens) ? batch - done : kTokens;
-        hipLaunchKernelGGL(gemv_mfma_kernel, dim3(blocks), dim3(kWaves * 64), 0, s, m.q,
-                           static_cast<const uint16_t*>(m.d), x + static_cast<uint64_t>(done) * m.cols,
-                           y + static_cast<uint64_t>(done) * m.rows, m.rows, m.cols, nt, wscale, inv);
+        const uint8_t* q = m.q;
+        const uint16_t* d = static_cast<const uint16_t*>(m.d);
+        const float* xp = x + static_cast<uint64_t>(done) * m.cols;
+        float* yp = y + static_cast<uint64_t>(done) * m.rows;
+        if (m.cols == 512)
+            hipLaunchKernelGGL(gemv_mfma_kernel<16>, dim3(blocks), dim3(kWaves * 64), 0, s, q, d, xp, yp, m.rows, nt, wscale, inv);
+        else
+            hipLaunchKernelGGL(gemv_mfma_kernel<32>, dim3(blocks), dim3(kWaves * 64), 0, s, q, d, xp, yp, m.rows, nt, wscale, inv);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -32,8 +32,8 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
                        uint32_t batch, float* workspace, hipStream_t stream);
 
 // Batched product on the matrix cores with f16 operands (Q8_0 with f16
-// scales, cols a multiple of 256 up to 1024, any batch): returns
-// hipErrorNotSupported for other matrices, which then take launch_gemm.
+// scales, cols 512 or 1024, any batch): returns hipErrorNotSupported for
+// other matrices, which then take launch_gemm.
 hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
                             hipStream_t stream);
 
