@@ -179,6 +179,22 @@ def test_gemm_small_full(wt, sf, R, C, B):
         Q.qmv_destroy(h)
 
 
+# Large-batch GEMM shapes (batch >= 128): ragged rows and tokens, odd step
+# counts, and a split K whose slices have different step counts.
+@pytest.mark.parametrize("wt,sf", [(1, 0), (1, 1), (2, 0), (2, 1)])
+@pytest.mark.parametrize("R,C,B", [(300, 384, 129), (1000, 640, 200), (256, 3200, 130),
+                                   (513, 1152, 333)])
+def test_gemm_large_batch_shapes(wt, sf, R, C, B):
+    img = K.make_image(420 + B, R, wt, sf, R, C, lo=-1e-2)
+    h = K.upload(img, wt, sf, R, C)
+    try:
+        xb = K.make_xb(420 + B, R + 2, B, C)
+        ref, norm = O.product(img, wt, sf, R, C, xb, threads=K.THREADS)
+        close(K.gpu_gemm(h, xb), ref, norm, f"gemm-large {wt}/{sf} {R}x{C} b{B}")
+    finally:
+        Q.qmv_destroy(h)
+
+
 # ---- embedding gather -------------------------------------------------------
 
 @pytest.mark.parametrize("wt,sf", [(1, 0), (1, 1), (2, 0), (2, 1)])
