@@ -68,6 +68,16 @@ def lib():
         L.orc_class_wtype.restype = i32
         L.orc_check_image.argtypes = [u32, u32, u64, u64, vp, u64]
         L.orc_check_image.restype = i32
+        L.orc_gguf_span.argtypes = [u32, u64, u64, ctypes.POINTER(u64)]
+        L.orc_gguf_span.restype = i32
+        L.orc_check_gguf.argtypes = [u32, u64, u64, vp, u64]
+        L.orc_check_gguf.restype = i32
+        L.orc_gguf_to_image.argtypes = [u32, u64, u64, vp, vp]
+        L.orc_gguf_to_image.restype = i32
+        L.orc_f16_bits.argtypes = [ctypes.c_float]
+        L.orc_f16_bits.restype = ctypes.c_uint16
+        L.orc_quantize_weights.argtypes = [u32, u32, u64, u64, vp, vp]
+        L.orc_quantize_weights.restype = i32
         _lib = L
     return _lib
 
@@ -208,3 +218,56 @@ def within_tolerance(y, ref, norm, rel: float = 2e-3):
     pos = norm > 0
     worst = float((err[pos] / norm[pos]).max()) if pos.any() else 0.0
     return ok, worst
+
+
+# ---- GGUF block data (the minfer GGUF page's BlockQ4_0 / BlockQ8_0) ----
+
+def gguf_span(wtype, rows, cols):
+    """(outcome, bytes): rows * cols / 32 blocks of 18 (Q4_0) or 34 (Q8_0)."""
+    out = ctypes.c_uint64(0)
+    st = lib().orc_gguf_span(wtype, rows, cols, ctypes.byref(out))
+    return OUTCOME[st], (out.value if st == 0 else None)
+
+
+def check_gguf(wtype, rows, cols, src, nbytes=None) -> str:
+    a = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    n = a.size if nbytes is None else nbytes
+    return OUTCOME[lib().orc_check_gguf(wtype, rows, cols, _ptr(a), n)]
+
+
+def gguf_to_image(wtype, rows, cols, src) -> np.ndarray:
+    """The .mlb image (f16 scales, both pads) holding the GGUF blocks' weights."""
+    st, s = span(wtype, 1, rows, cols)
+    if st != "ok":
+        raise ValueError(f"span: {st}")
+    a = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    ok, need = gguf_span(wtype, rows, cols)
+    if ok != "ok" or a.size < need:
+        raise ValueError("gguf data too short")
+    img = np.zeros(s["full_span"], dtype=np.uint8)
+    st = lib().orc_gguf_to_image(wtype, rows, cols, _ptr(a), _ptr(img))
+    if st != 0:
+        raise ValueError(OUTCOME[st])
+    return img
+
+
+# ---- weight writer (the .mlb page's quantization rules) ----
+
+def f16_bits(x: float) -> int:
+    """The oracle's own float32 -> binary16 rounding (nearest even)."""
+    return int(lib().orc_f16_bits(float(np.float32(x))))
+
+
+def quantize_weights(wtype, scale_f16, rows, cols, w: np.ndarray):
+    """(outcome, image): the full_span .mlb bytes of float32 w [rows][cols]
+    quantized by the writer's rule; outcome 'format' when a scale does not
+    fit f16 (image None)."""
+    st, s = span(wtype, scale_f16, rows, cols)
+    if st != "ok":
+        return st, None
+    wf = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    if wf.size != rows * cols:
+        raise ValueError("w has the wrong size")
+    img = np.zeros(s["full_span"], dtype=np.uint8)
+    st = lib().orc_quantize_weights(wtype, scale_f16, rows, cols, _ptr(wf), _ptr(img))
+    return OUTCOME[st], (img if st == 0 else None)

@@ -327,3 +327,210 @@ int orc_check_image(uint32_t wtype, uint32_t scale_f16, uint64_t rows,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * GGUF block data (minfer, "GGUF load" page, section "Quantized sizing: 32
+ * values in 18 bytes"): a Q4_0 or Q8_0 tensor is a run of blocks, each an
+ * f16 scale d followed by the block's quants - BlockQ4_0 { d: f16,
+ * qs: 16 bytes } (18 bytes), BlockQ8_0 { d: f16, qs: 32 int8 } (34 bytes);
+ * the tensor's size is its element count / 32 x the block size.
+ * Readings (the page names the blocks but not these points): the blocks are
+ * in the same row-major order as the .mlb arrays (a tensor's first dimension
+ * is the row length, so block k covers row k / (C/32)); the scale is
+ * little-endian; and the 16 Q4_0 bytes hold their 32 elements in the .mlb
+ * page's nibble order (byte j: element j low, element j + 16 high).
+ * ---------------------------------------------------------------------- */
+
+/* bytes[0] = rows * cols / 32 * (18 | 34), overflow-checked. */
+int orc_gguf_span(uint32_t wtype, uint64_t rows, uint64_t cols, uint64_t *bytes) {
+    if (wtype != ORC_Q8_0 && wtype != ORC_Q4_0) return ORC_FORMAT;
+    if (rows == 0 || cols == 0 || cols % 32 != 0) return ORC_SHAPE;
+    if (rows > ORC_DIM_LIMIT || cols > ORC_DIM_LIMIT) return ORC_SHAPE;
+    uint64_t blocks = rows * (cols / 32); /* <= 2^43: no overflow */
+    uint64_t bsize = (wtype == ORC_Q8_0) ? 34 : 18;
+    if (blocks > UINT64_MAX / bsize) return ORC_SHAPE;
+    *bytes = blocks * bsize;
+    return ORC_OK;
+}
+
+/* The loader's checks on GGUF block data: long enough, no Q8_0 quant byte
+ * of -128 (the .mlb rule, applied to the matrix whatever file holds it). */
+int orc_check_gguf(uint32_t wtype, uint64_t rows, uint64_t cols,
+                   const uint8_t *src, uint64_t nbytes) {
+    uint64_t need;
+    int st = orc_gguf_span(wtype, rows, cols, &need);
+    if (st != ORC_OK) return st;
+    if (src == NULL) return ORC_ARG;
+    if (nbytes < need) return ORC_FORMAT;
+    if (wtype == ORC_Q8_0) {
+        uint64_t blocks = need / 34;
+        for (uint64_t k = 0; k < blocks; ++k)
+            for (int j = 0; j < 32; ++j)
+                if (src[34 * k + 2 + j] == 0x80) return ORC_FORMAT;
+    }
+    return ORC_OK;
+}
+
+/* The .mlb image (q array, zero pad, f16 d array, zero pad; full_span
+ * bytes, scale_f16 = 1) holding the same weights as the GGUF blocks. */
+int orc_gguf_to_image(uint32_t wtype, uint64_t rows, uint64_t cols,
+                      const uint8_t *src, uint8_t *img) {
+    uint64_t span[5], need;
+    int st = orc_span(wtype, 1, rows, cols, span);
+    if (st != ORC_OK) return st;
+    st = orc_gguf_span(wtype, rows, cols, &need);
+    if (st != ORC_OK) return st;
+    memset(img, 0, span[4]);
+    uint64_t qb = (wtype == ORC_Q8_0) ? 32 : 16, bsize = 2 + qb;
+    uint64_t blocks = rows * (cols / 32);
+    for (uint64_t k = 0; k < blocks; ++k) {
+        const uint8_t *b = src + k * bsize;
+        memcpy(img + k * qb, b + 2, qb);            /* quants of block k */
+        memcpy(img + span[1] + 2 * k, b, 2);        /* its f16 scale */
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Weight writer (the .mlb page, "Quantization rule" and the two paragraphs
+ * after it), per block of 32 consecutive weights of a row, in float32
+ * operations rounded one at a time:
+ *   - Q8_0, f32 scales: the quantization rule itself (orc_quantize_q8);
+ *   - Q8_0, f16 scales: d = amax / 127 rounded to the nearest f16, then
+ *     q = trunc(x * (1 / d) + copysign(0.5, x)) against that rounded d,
+ *     clamped to [-127, 127]; a d above 65504 cannot be stored and is
+ *     refused;
+ *   - Q4_0, "round" rule (the rounding the page attributes to llama.cpp):
+ *     d = (the element of largest magnitude) / -8, level =
+ *     trunc(x * (1 / d) + 8.5), at most 15, stored as the nibble; with f16
+ *     scales d is stored rounded to f16.
+ * Readings (the page leaves these open): the element of largest magnitude
+ * is the first one reaching it; a Q4_0 block with d = 0 uses 1 / d = 0
+ * (every nibble 8, every weight 0), as llama.cpp does; the Q4_0 levels use
+ * the float32 d also when the stored scale is its f16 rounding (only the
+ * Q8_0 sentence says "against that rounded d"); an f16 Q8_0 scale that
+ * rounds to 0 from amax >= 1e-30 gives q = 0 (every weight is 0 either
+ * way); the f16 rounding is the oracle's own round-to-nearest-even of the
+ * float32 value; a Q4_0 f16 scale above 65504 is refused like a Q8_0 one.
+ * The least-squares Q4_0 search is not written.
+ * Returns ORC_OK, ORC_SHAPE / ORC_FORMAT as orc_span, or ORC_FORMAT for a
+ * scale that does not fit f16 (then img is unspecified).  img receives
+ * full_span bytes (both pads zero).
+ * ---------------------------------------------------------------------- */
+
+/* float32 -> IEEE binary16 bits, round to nearest even (finite inputs and
+ * infinities; NaN becomes a quiet NaN). */
+uint16_t orc_f16_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t ex = (u >> 23) & 0xFFu, man = u & 0x7FFFFFu;
+    if (ex == 0xFF) return (uint16_t)(sign | 0x7C00u | (man ? 0x200u : 0u));
+    /* value = 1.man x 2^(ex - 127) for normal f32; f16 normal exponent range
+     * is [-14, 15], subnormals step 2^-24 */
+    int e = (int)ex - 127;
+    if (ex == 0) return sign; /* f32 subnormals are far below f16's range */
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    /* integer significand with the implicit bit: m24 = 1.man x 2^23 */
+    uint32_t m24 = man | 0x800000u;
+    /* the f16 result, in units of its last place: shift right by s bits */
+    int s = (e >= -14) ? 13 : 13 + (-14 - e); /* normals keep 10 bits */
+    if (s > 24) return sign;                   /* below half the smallest subnormal */
+    uint32_t q = m24 >> s, rem = m24 & ((1u << s) - 1u), half = 1u << (s - 1);
+    if (rem > half || (rem == half && (q & 1u))) ++q;
+    if (e >= -14) {
+        /* q in [2^10, 2^11]; 2^11 carries into the exponent */
+        int E = e + 15;
+        if (q == 0x800u) { q = 0x400u; ++E; }
+        if (E > 30) return (uint16_t)(sign | 0x7C00u);
+        return (uint16_t)(sign | (uint16_t)(E << 10) | (uint16_t)(q & 0x3FFu));
+    }
+    /* subnormal (q may round up to 0x400, the smallest normal: same bits) */
+    return (uint16_t)(sign | (uint16_t)q);
+}
+
+static float orc_trunc_clamp(float u, float lo, float hi) {
+    float t = truncf(u);
+    if (t > hi) return hi;
+    if (t < lo) return lo;
+    return t;
+}
+
+int orc_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint64_t rows,
+                         uint64_t cols, const float *w, uint8_t *img) {
+    uint64_t span[5];
+    int st = orc_span(wtype, scale_f16, rows, cols, span);
+    if (st != ORC_OK) return st;
+    memset(img, 0, span[4]);
+    uint64_t nblk = rows * (cols / 32);
+    uint8_t *dptr = img + span[1];
+    for (uint64_t k = 0; k < nblk; ++k) {
+        const float *x = w + 32 * k;
+        float dstore; /* the scale as stored (f32 path), or its f16 value */
+        uint16_t dbits16 = 0;
+        if (wtype == ORC_Q8_0) {
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                float a = fabsf(x[j]);
+                if (a > amax) amax = a;
+            }
+            int8_t *q = (int8_t *)img + 32 * k;
+            if (amax < 1e-30f) {
+                dstore = 0.0f;
+                for (int j = 0; j < 32; ++j) q[j] = 0;
+            } else if (!scale_f16) {
+                dstore = amax / 127.0f;
+                float id = 127.0f / amax;
+                for (int j = 0; j < 32; ++j) {
+                    volatile float t = x[j] * id;
+                    float u = t + copysignf(0.5f, x[j]);
+                    q[j] = (int8_t)(int)orc_trunc_clamp(u, -127.0f, 127.0f);
+                }
+            } else {
+                float d32 = amax / 127.0f;
+                dbits16 = orc_f16_bits(d32);
+                if ((dbits16 & 0x7FFFu) >= 0x7C00u) return ORC_FORMAT; /* > 65504 */
+                float d16 = (float)orc_f16_value(dbits16);
+                if (d16 == 0.0f) {
+                    for (int j = 0; j < 32; ++j) q[j] = 0;
+                } else {
+                    float id = 1.0f / d16;
+                    for (int j = 0; j < 32; ++j) {
+                        volatile float t = x[j] * id;
+                        float u = t + copysignf(0.5f, x[j]);
+                        q[j] = (int8_t)(int)orc_trunc_clamp(u, -127.0f, 127.0f);
+                    }
+                }
+                dstore = d16;
+            }
+        } else {
+            float amax = 0.0f, mx = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                float a = fabsf(x[j]);
+                if (a > amax) { amax = a; mx = x[j]; }
+            }
+            float d = mx / -8.0f;
+            float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+            uint8_t *qb = img + 16 * k;
+            for (int j = 0; j < 16; ++j) {
+                volatile float t0 = x[j] * id, t1 = x[j + 16] * id;
+                float l0 = truncf(t0 + 8.5f), l1 = truncf(t1 + 8.5f);
+                if (l0 > 15.0f) l0 = 15.0f;
+                if (l1 > 15.0f) l1 = 15.0f;
+                qb[j] = (uint8_t)((unsigned)l0 | ((unsigned)l1 << 4));
+            }
+            if (scale_f16) {
+                dbits16 = orc_f16_bits(d);
+                if ((dbits16 & 0x7FFFu) >= 0x7C00u) return ORC_FORMAT;
+            }
+            dstore = d;
+        }
+        if (scale_f16) {
+            dptr[2 * k] = (uint8_t)(dbits16 & 0xFFu);
+            dptr[2 * k + 1] = (uint8_t)(dbits16 >> 8);
+        } else {
+            memcpy(dptr + 4 * k, &dstore, 4);
+        }
+    }
+    return ORC_OK;
+}

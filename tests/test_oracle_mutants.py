@@ -93,3 +93,52 @@ def test_planted_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
         except Exception as e:  # noqa: BLE001 - any failure of a pin counts
             failed.append(fn.__name__)
     assert failed, f"no pin catches: {name}"
+
+
+# ---- the GGUF reader and the weight writer ----------------------------------
+
+import test_oracle_writer_gguf as W  # noqa: E402
+
+MUTANTS_WG = [
+    ("gguf quants read from the scale", "memcpy(img + k * qb, b + 2, qb);",
+     "memcpy(img + k * qb, b, qb);"),
+    ("gguf Q8 block of 32 bytes", "uint64_t bsize = (wtype == ORC_Q8_0) ? 34 : 18;",
+     "uint64_t bsize = (wtype == ORC_Q8_0) ? 32 : 18;"),
+    ("gguf -128 not rejected", "if (src[34 * k + 2 + j] == 0x80) return ORC_FORMAT;", "(void)0;"),
+    ("writer f16 quants against the unrounded scale", "float id = 1.0f / d16;",
+     "float id = 127.0f / amax;"),
+    ("writer f16 overflow not refused",
+     "if ((dbits16 & 0x7FFFu) >= 0x7C00u) return ORC_FORMAT; /* > 65504 */", ""),
+    ("writer Q4 unsigned maximum", "if (a > amax) { amax = a; mx = x[j]; }",
+     "if (a > amax) { amax = a; mx = a; }"),
+    ("writer Q4 offset 8.0", "float l0 = truncf(t0 + 8.5f), l1 = truncf(t1 + 8.5f);",
+     "float l0 = truncf(t0 + 8.0f), l1 = truncf(t1 + 8.0f);"),
+    ("writer Q4 nibbles swapped", "qb[j] = (uint8_t)((unsigned)l0 | ((unsigned)l1 << 4));",
+     "qb[j] = (uint8_t)((unsigned)l1 | ((unsigned)l0 << 4));"),
+    ("writer Q4 scale +8", "float d = mx / -8.0f;", "float d = mx / 8.0f;"),
+    ("f16 rounding truncates", "if (rem > half || (rem == half && (q & 1u))) ++q;", "(void)0;"),
+    ("f16 ties away from zero", "if (rem > half || (rem == half && (q & 1u))) ++q;",
+     "if (rem >= half) ++q;"),
+]
+
+
+def _pins_wg():
+    return [(W.test_gguf_sizes_printed_on_page, ()), (W.test_gguf_hand_built_blocks, ()),
+            (W.test_gguf_round_trip_is_the_two_array_image, (O.Q8_0,)),
+            (W.test_gguf_round_trip_is_the_two_array_image, (O.Q4_0,)),
+            (W.test_gguf_checks, ()), (W.test_f16_rounding_matches_numpy, ()),
+            (W.test_q8_f32_writer_is_the_activation_quantizer, ()),
+            (W.test_q8_f16_writer_closed_forms, ()), (W.test_q8_f16_writer_properties, ()),
+            (W.test_q4_round_writer_exact_recovery, ()), (W.test_q4_round_writer_properties, ())]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_WG, ids=[m[0] for m in MUTANTS_WG])
+def test_planted_writer_or_gguf_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    _install(tmp_path, monkeypatch, old, new)
+    failed = []
+    for fn, args in _pins_wg():
+        try:
+            fn(*args)
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(fn.__name__)
+    assert failed, f"no pin catches: {name}"
