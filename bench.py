@@ -12,8 +12,9 @@ bracketed by device synchronisation and HIP events on the launching stream.
 Default workload: Q4_0 GEMV, 4096 x 4096, f16 scales, batch 1.  Other
 workloads (--workload): q8_gemv_512, decode_layer (wq|wk|wv and w1|w3 grouped
 on their shared inputs), decode_layer_7 (one launch per matrix), gemm_q4_14336x4096,
-gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, and copy (a plain
-device copy, used to calibrate HBM byte counters).
+gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, writer_q4_14336x4096
+(the weight writer: float32 weights to a Q4_0 f16-scale image by the round
+rule), and copy (a plain device copy, used to calibrate HBM byte counters).
 """
 from __future__ import annotations
 
@@ -67,6 +68,9 @@ def workload(name):
     if name == "gemm_q8_4096x14336":
         return ("prefill GEMM Q8_0 4096x14336 f32 scales x bf16 [512x14336]", "gemm", 4,
                 [(1, Q8, 0, 4096, 14336)], 512)
+    if name == "writer_q4_14336x4096":
+        return ("weight writer: float32 14336x4096 -> Q4_0 f16 scales (round rule)", "writer", 4,
+                [(0, Q4, 1, 14336, 4096)], 1)
     if name in ("lm_head_b1", "lm_head_b64"):
         b = 1 if name.endswith("b1") else 64
         return (f"shared-classifier LM head Q8_0 248320x1024 f16 scales, f32 hidden, "
@@ -94,6 +98,7 @@ DOMINANT_KERNEL = {
     "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm.hip"),
     "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
     "embed_64": ("embed_kernel", "misc.hip"),
+    "writer_q4_14336x4096": ("quantize_q4_round_kernel", "writer.hip"),
 }
 
 
@@ -128,6 +133,8 @@ def step_work(kind, mats, batch, groups=None):
         elif kind == "gemm":
             byts += w + 2 * c * batch + 4 * r * batch
             flops += 2 * r * c * batch
+        elif kind == "writer":
+            byts += 4 * r * c + w          # float32 weights in, the image out
         elif kind == "embed":
             byts += batch * (matrix_bytes(wt, sf, 1, c)) + 4 * batch + 4 * batch * c
     return byts, flops
@@ -145,6 +152,14 @@ def make_image(config, m, wt, sf, r, c):
     img[:sp["q_bytes"]] = q.view(np.uint8)
     img[sp["d_offset"]:] = d.view(np.uint8)
     return img
+
+
+def writer_weights(config, m, r, c):
+    """float32 weights for the writer workload: N(0,1) values drawn from the
+    matrix's seeded activation stream."""
+    from block_quant_weight_amd import synth
+    g = synth.rng(config, m, synth.STREAM_ACT)
+    return synth.act_f32(g, r, c)
 
 
 def kernel_source_hash(src):
@@ -187,6 +202,21 @@ def cpu_baseline(kind, config, mats, batch, budget_s):
         b, _ = step_work(kind, mats[:1], batch)
         return {"value": reps * b / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"{reps} gathers of {batch} rows, single thread"}
+    if kind == "writer":
+        w = writer_weights(config, m, r, c)
+        n_rows = 64
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            lo = (reps * n_rows) % (r - n_rows)
+            O.quantize_weights(wt, sf, n_rows, c, w[lo:lo + n_rows])
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= 0.5 * budget_s or reps >= 10000:
+                break
+        byts = reps * n_rows * c * 4 + reps * n_rows * matrix_bytes(wt, sf, 1, c)
+        return {"value": byts / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{reps} x {n_rows} rows of {r} (single thread, {el:.1f} s)"}
     if kind == "gemm":
         x = synth.act_bf16(synth.rng(config, m, synth.STREAM_ACT), batch, c)
     else:
@@ -261,6 +291,10 @@ def main():
         ms = e0.elapsed_time(e1) / 10
         print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n,
                           "ms_per_copy": ms, "GB/s": 2 * n / ms / 1e6}))
+        return
+
+    if kind == "writer":
+        run_writer(args, desc, config, mats, stream)
         return
 
     groups = launch_groups(args.workload, mats)
@@ -443,6 +477,72 @@ def main():
         "dtype": dtype, "data": "synthetic (seeded; uniform quants and scales, N(0,1) "
                                 "activations)",
         "config": wl, "roofline": roof, "cpu_baseline": cpu}), flush=True)
+
+
+def run_writer(args, desc, config, mats, stream):
+    """The weight writer as a step: one qmv_quantize_weights call over a
+    float32 matrix (rotated copies, >= 512 MB), captured in a graph."""
+    import torch
+    from block_quant_weight_amd import qmv as Q
+    m, wt, sf, r, c = mats[0]
+    step_bytes, _ = step_work("writer", mats, 1)
+    w = torch.from_numpy(writer_weights(config, m, r, c)).cuda()
+    ncopies = max(2, -(-ROTATE_BYTES // (4 * r * c)))
+    ws = [w] + [w.clone() for _ in range(ncopies - 1)]
+    n = Q.qmv_span(wt, sf, r, c)["min_span"]
+    image = torch.empty(n, dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 20
+    log(f"workload {args.workload}: {desc}; {ncopies} input copies; "
+        f"{steps} steps after {warmup} warm-up")
+    for i in range(warmup):
+        Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+    torch.cuda.synchronize()
+    if int(status[0].item()) != 0:
+        raise RuntimeError("writer reported an unstorable scale")
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    if use_graph:
+        g.replay()
+    else:
+        for i in range(steps):
+            Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    kname, ksrc = DOMINANT_KERNEL[args.workload]
+    roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
+            "launch": {"algorithmic_bytes_per_launch": step_bytes,
+                       "us_per_launch": round(ms_step * 1e3, 3)},
+            "launches_per_step": 1, "algorithmic_bytes_per_step": step_bytes,
+            "flops_per_step": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores")
+        cpu = cpu_baseline("writer", config, mats, 1, args.cpu_budget)
+    wl = {"workload": args.workload, "description": desc, "batch": 1,
+          "matrices": [{"wtype": "Q8_0" if wt == Q8 else "Q4_0", "scales": "f16" if sf else "f32",
+                        "rows": r, "cols": c}],
+          "input_copies_rotated": ncopies, "hip_graph": use_graph}
+    print(json.dumps({
+        "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; N(0,1) float32 weights)", "config": wl,
+        "roofline": roof, "cpu_baseline": cpu}), flush=True)
 
 
 if __name__ == "__main__":

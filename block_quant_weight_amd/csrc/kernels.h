@@ -41,6 +41,18 @@ hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t
 hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,
                         float* out, hipStream_t stream);
 
+// GGUF Q4_0 / Q8_0 blocks (f16 scale, then quants; 2-byte aligned at src)
+// repacked: block k's quants to q + k * (16 | 32), its scale to d[k].
+hipError_t launch_gguf_repack(uint32_t wtype, const void* src, uint64_t nblocks, uint8_t* q,
+                              uint16_t* d, hipStream_t stream);
+
+// Writer rules over nblocks blocks of float32 weights w: quants to q, then
+// q_pad (< 64) zero bytes, scales to d (float or f16 bits); *bad cleared,
+// then set to 1 when an f16 scale does not fit.  Kernels only (no memset).
+hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, const float* w,
+                                   uint64_t nblocks, uint8_t* q, uint32_t q_pad, void* d,
+                                   uint32_t* bad, hipStream_t stream);
+
 // Activation Q8_0 quantizer over n floats (n % 32 == 0).
 hipError_t launch_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,
                               hipStream_t stream);

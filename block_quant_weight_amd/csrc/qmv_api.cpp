@@ -139,6 +139,48 @@ int qmv_upload(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
     return QMV_OK;
 }
 
+int qmv_upload_gguf(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
+    if (h == nullptr || src == nullptr) return QMV_E_ARG;
+    if (h->dev != nullptr) return QMV_E_ARG;  // uploaded once, then read-only
+    const qmv::Layout& L = h->layout;
+    if (L.scale_f16 != 1) return QMV_E_FORMAT;  // GGUF Q4_0 / Q8_0 scales are f16
+    int st = qmv::check_gguf(L, src, nbytes);
+    if (st != QMV_OK) return st;
+    uint64_t gb = 0;
+    st = qmv::gguf_bytes(L.wtype, L.rows, L.cols, &gb);
+    if (st != QMV_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return QMV_E_DEVICE;
+    void* img = nullptr;
+    void* raw = nullptr;
+    hipError_t e = hipMalloc(&img, L.full_span);
+    if (e != hipSuccess) return device_status(e);
+    e = hipMalloc(&raw, gb);
+    if (e != hipSuccess) {
+        (void)hipFree(img);
+        return device_status(e);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* d = static_cast<uint8_t*>(img);
+    // the raw blocks to the device, the image zeroed (its padding), then
+    // each block's quants and scale moved to the two arrays
+    e = hipMemcpyAsync(raw, src, gb, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemsetAsync(img, 0, L.full_span, s);
+    if (e == hipSuccess)
+        e = qmv::launch_gguf_repack(L.wtype, raw, uint64_t{L.rows} * (L.cols / 32), d,
+                                    reinterpret_cast<uint16_t*>(d + L.d_offset), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    (void)hipFree(raw);
+    if (e != hipSuccess) {
+        (void)hipFree(img);
+        return device_status(e);
+    }
+    h->dev = d;
+    h->device = dev;
+    h->dexp = qmv::scale_exponent_gguf(L, src);
+    return QMV_OK;
+}
+
 int qmv_destroy(qmv_handle h) {
     if (h == nullptr) return QMV_OK;
     if (h->dev != nullptr) {
@@ -202,6 +244,22 @@ int qmv_embed_rows(qmv_handle h, const int32_t* ids, uint32_t n, float* out,
     if (!aligned16(ids) || !aligned16(out)) return QMV_E_ARG;
     return device_status(qmv::launch_embed(view(h), ids, n, out,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
+                         const float* w, void* image, uint64_t image_bytes, uint32_t* status,
+                         void* stream) {
+    qmv::Layout L;
+    int st = qmv::compute_layout(wtype, scale_f16, rows, cols, &L);
+    if (st != QMV_OK) return st;
+    if (w == nullptr || image == nullptr || status == nullptr) return QMV_E_ARG;
+    if (!aligned16(w) || !aligned16(image) || image_bytes < L.min_span) return QMV_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return QMV_E_ARG;
+    uint8_t* img = static_cast<uint8_t*>(image);
+    return device_status(qmv::launch_quantize_weights(
+        wtype, scale_f16, w, uint64_t{rows} * (cols / 32), img,
+        static_cast<uint32_t>(L.d_offset - L.q_bytes), img + L.d_offset, status,
+        static_cast<hipStream_t>(stream)));
 }
 
 int qmv_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,

@@ -84,6 +84,62 @@ int check_bytes(const Layout& L, const void* src, uint64_t nbytes) {
     return QMV_OK;
 }
 
+int gguf_bytes(uint32_t wtype, uint32_t rows, uint32_t cols, uint64_t* bytes) {
+    Layout L;
+    const int st = compute_layout(wtype, 1, rows, cols, &L);
+    if (st != QMV_OK) return st;
+    uint64_t n;
+    if (!mul_ok(uint64_t{rows} * (cols / 32), wtype == QMV_Q8_0 ? 34 : 18, &n)) return QMV_E_SHAPE;
+    *bytes = n;
+    return QMV_OK;
+}
+
+int check_gguf(const Layout& L, const void* src, uint64_t nbytes) {
+    if (src == nullptr) return QMV_E_ARG;
+    uint64_t need;
+    const int st = gguf_bytes(L.wtype, L.rows, L.cols, &need);
+    if (st != QMV_OK) return st;
+    if (nbytes < need) return QMV_E_FORMAT;
+    if (L.wtype == QMV_Q8_0) {
+        const uint8_t* p = static_cast<const uint8_t*>(src);
+        const uint64_t blocks = need / 34;
+        for (uint64_t k = 0; k < blocks; ++k) {
+            const uint8_t* b = p + 34 * k + 2;
+            for (int j = 0; j < 32; ++j)
+                if (b[j] == 0x80) return QMV_E_FORMAT;
+        }
+    }
+    return QMV_OK;
+}
+
+namespace {
+// exponent of the largest of the f16 magnitudes (low 15 bits) m
+int32_t f16_max_exponent(uint16_t m) {
+    if (m >= 0x7C00) return 0;  // inf or NaN
+    const int e = m >> 10, f = m & 0x3FF;
+    const float amax = e == 0 ? std::ldexp(static_cast<float>(f), -24)
+                              : std::ldexp(static_cast<float>(1024 + f), e - 25);
+    if (amax == 0.f) return 0;
+    int ex = 0;
+    (void)std::frexp(amax, &ex);
+    return ex;
+}
+}  // namespace
+
+int32_t scale_exponent_gguf(const Layout& L, const void* src) {
+    const uint8_t* p = static_cast<const uint8_t*>(src);
+    const uint64_t blocks = uint64_t{L.rows} * (L.cols / 32);
+    const uint64_t bsize = L.wtype == QMV_Q8_0 ? 34 : 18;
+    uint16_t m = 0;
+    for (uint64_t k = 0; k < blocks; ++k) {
+        uint16_t b;
+        __builtin_memcpy(&b, p + k * bsize, 2);
+        b &= 0x7FFF;
+        m = b > m ? b : m;
+    }
+    return f16_max_exponent(m);
+}
+
 int32_t scale_exponent(const Layout& L, const void* src) {
     const uint8_t* d = static_cast<const uint8_t*>(src) + L.d_offset;
     const uint64_t n = L.d_bytes / (L.scale_f16 ? 2 : 4);
@@ -133,6 +189,11 @@ int qmv_span(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
     if (d_bytes) *d_bytes = L.d_bytes;
     if (min_span) *min_span = L.min_span;
     return QMV_OK;
+}
+
+int qmv_gguf_span(uint32_t wtype, uint32_t rows, uint32_t cols, uint64_t* bytes) {
+    if (bytes == nullptr) return QMV_E_ARG;
+    return qmv::gguf_bytes(wtype, rows, cols, bytes);
 }
 
 int qmv_class_wtype(uint32_t file_wtype, uint32_t q8_mask, uint32_t class_bit,

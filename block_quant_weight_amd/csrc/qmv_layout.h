@@ -20,6 +20,18 @@ int compute_layout(uint32_t wtype, uint32_t scale_f16, uint32_t rows,
 // Q8_0 quant equal to -128.  QMV_OK, QMV_E_ARG or QMV_E_FORMAT.
 int check_bytes(const Layout& L, const void* src, uint64_t nbytes);
 
+// GGUF block data of a Q4_0 / Q8_0 matrix: rows * cols / 32 blocks of 18 /
+// 34 bytes (an f16 scale, then the quants).  QMV_OK or QMV_E_FORMAT /
+// QMV_E_SHAPE; *bytes on success.
+int gguf_bytes(uint32_t wtype, uint32_t rows, uint32_t cols, uint64_t* bytes);
+
+// Checks GGUF block data for a matrix of layout L (f16 scales): long enough,
+// no Q8_0 quant equal to -128.  QMV_OK, QMV_E_ARG or QMV_E_FORMAT.
+int check_gguf(const Layout& L, const void* src, uint64_t nbytes);
+
+// scale_exponent for GGUF block data (the scale of block k at k * 18 / 34).
+int32_t scale_exponent_gguf(const Layout& L, const void* src);
+
 // Binary exponent E of the largest scale magnitude of a checked buffer
 // (max |d| in [2^(E-1), 2^E)); 0 when every scale is zero or some scale is
 // inf or NaN.  Kernels that hold weights in a narrow float type scale them

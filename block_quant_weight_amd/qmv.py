@@ -22,7 +22,8 @@ QMV_E_NOMEM = -5
 # every symbol include/qmv.h declares
 EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
-           "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str")
+           "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
+           "qmv_upload_gguf", "qmv_quantize_weights")
 
 _lib = None
 
@@ -55,6 +56,9 @@ def lib():
             "qmv_quantize_q8": ([vp, u64, vp, vp, vp], i32),
             "qmv_block_dots": ([vp, vp, vp, vp], i32),
             "qmv_status_str": ([i32], ctypes.c_char_p),
+            "qmv_gguf_span": ([u32, u32, u32, pu64], i32),
+            "qmv_upload_gguf": ([vp, vp, u64, vp], i32),
+            "qmv_quantize_weights": ([u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -115,6 +119,13 @@ def qmv_span(wtype, scale_f16, rows, cols):
     return dict(zip(("q_bytes", "d_offset", "d_bytes", "min_span"), (o.value for o in out)))
 
 
+def qmv_gguf_span(wtype, rows, cols) -> int:
+    """Bytes of a Q4_0 / Q8_0 tensor's GGUF block data; raises QmvError."""
+    out = ctypes.c_uint64(0)
+    _check(lib().qmv_gguf_span(wtype, rows, cols, ctypes.byref(out)), "qmv_gguf_span")
+    return out.value
+
+
 def qmv_class_wtype(file_wtype, q8_mask, class_bit, shared_classifier=0) -> int:
     out = ctypes.c_uint32(0)
     _check(lib().qmv_class_wtype(file_wtype, q8_mask, class_bit, shared_classifier,
@@ -140,6 +151,44 @@ def qmv_upload(h: QmvHandle, src, nbytes=None, stream=None):
         raise ValueError("nbytes exceeds the buffer")
     st = lib().qmv_upload(h.ptr, a.ctypes.data_as(ctypes.c_void_p), n, _stream(stream))
     _check(st, "qmv_upload")
+
+
+def qmv_upload_gguf(h: QmvHandle, src, nbytes=None, stream=None):
+    """src: a host buffer holding the matrix's GGUF block data."""
+    import numpy as np
+    a = np.ascontiguousarray(np.frombuffer(src, dtype=np.uint8)
+                             if isinstance(src, (bytes, bytearray, memoryview))
+                             else np.asarray(src).view(np.uint8).reshape(-1))
+    n = a.size if nbytes is None else int(nbytes)
+    if n > a.size:
+        raise ValueError("nbytes exceeds the buffer")
+    st = lib().qmv_upload_gguf(h.ptr, a.ctypes.data_as(ctypes.c_void_p), n, _stream(stream))
+    _check(st, "qmv_upload_gguf")
+
+
+def qmv_quantize_weights(wtype, scale_f16, w, image, status=None, stream=None):
+    """w: float32 [rows, cols] on the GPU; image: uint8 GPU tensor of at least
+    min_span bytes, receiving the .mlb bytes.  With status (an int32/uint32
+    GPU tensor of >= 1 element) the call only enqueues work and status[0]
+    tells, once done, whether a scale did not fit f16 (1); without it the
+    call waits and raises QmvError(QMV_E_FORMAT) in that case."""
+    import torch
+    rows, cols = w.shape
+    pw = _dev(w, torch.float32, rows * cols, "w")
+    if image.dtype != torch.uint8:
+        raise TypeError("image must be uint8")
+    pi = _dev(image, torch.uint8, 0, "image")
+    own = status is None
+    if own:
+        status = torch.empty(1, dtype=torch.int32, device=image.device)
+    ps = _dev(status, status.dtype, 1, "status")
+    st = lib().qmv_quantize_weights(wtype, scale_f16, rows, cols, pw, pi, image.numel(), ps,
+                                    _stream(stream))
+    _check(st, "qmv_quantize_weights")
+    if own:
+        torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+        if int(status[0].item()) != 0:
+            raise QmvError(QMV_E_FORMAT, "qmv_quantize_weights: a scale does not fit f16")
 
 
 def qmv_destroy(h: QmvHandle):

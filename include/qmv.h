@@ -115,6 +115,34 @@ int qmv_create(qmv_handle *out, uint32_t wtype, uint32_t scale_f16,
  */
 int qmv_upload(qmv_handle h, const void *src, uint64_t nbytes, void *stream);
 
+/*
+ * Size of a Q4_0 / Q8_0 tensor's data in a GGUF file, from the minfer page's
+ * "Quantized sizing: 32 values in 18 bytes": rows * cols / 32 blocks of 18
+ * bytes (BlockQ4_0: an f16 scale d, then 16 bytes of nibbles) or 34 bytes
+ * (BlockQ8_0: d, then 32 int8 quants).  Pure host arithmetic.
+ * Errors: QMV_E_ARG (bytes NULL), QMV_E_FORMAT (wtype), QMV_E_SHAPE (as
+ * qmv_span).
+ */
+int qmv_gguf_span(uint32_t wtype, uint32_t rows, uint32_t cols, uint64_t *bytes);
+
+/*
+ * Upload from GGUF block data instead of the two arrays: src holds the
+ * matrix's rows * cols / 32 blocks in row-major order (row r's blocks
+ * consecutive; a GGUF tensor's first dimension is the row length), each an
+ * f16 little-endian scale followed by the quants, the 16 Q4_0 bytes in the
+ * .mlb nibble order (byte j: element j low, element j + 16 high).  The
+ * blocks are copied to the device and repacked there, once, into the same
+ * image qmv_upload builds (q array, zero padding, f16 d array), so every
+ * compute call sees identical bytes.  The handle must have been created
+ * with scale_f16 = 1 (GGUF blocks carry f16 scales) and not yet uploaded.
+ * Checks, on the host: nbytes >= qmv_gguf_span and no Q8_0 quant byte equal
+ * to 0x80 (QMV_E_FORMAT).  Waits for `stream`; src may be released on
+ * return.  Allocates the image and a temporary device copy of src.
+ * Errors: QMV_E_ARG (null, second upload), QMV_E_FORMAT (f32-scale handle,
+ * short data, -128), QMV_E_NOMEM, QMV_E_DEVICE.
+ */
+int qmv_upload_gguf(qmv_handle h, const void *src, uint64_t nbytes, void *stream);
+
 /* Releases the handle and its device memory.  The caller makes sure no work
  * that reads it is still pending.  NULL is accepted.  Returns QMV_OK. */
 int qmv_destroy(qmv_handle h);
@@ -204,6 +232,36 @@ int qmv_embed_rows(qmv_handle h, const int32_t *ids, uint32_t n, float *out,
  */
 int qmv_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d,
                     void *stream);
+
+/*
+ * Weight writer: the .mlb image (q array, its zero padding, d array:
+ * min_span bytes as qmv_span gives them) of float32 weights w [rows][cols]
+ * (device memory), quantized per block of 32 by the rules of the .mlb
+ * page's "Quantization rule" section, in separate float32 operations:
+ *   - Q8_0, f32 scales: exactly qmv_quantize_q8 (the page uses one rule
+ *     for the writer and the activation quantizer);
+ *   - Q8_0, f16 scales: d = amax / 127 rounded to the nearest f16, then
+ *     q = trunc(x * (1 / d) + copysign(0.5, x)) against that rounded d,
+ *     clamped to [-127, 127] (q = 0 when d rounds to 0);
+ *   - Q4_0, the page's "round" rule: d = (the first element of largest
+ *     magnitude) / -8, nibble = min(15, trunc(x * (1 / d) + 8.5)) with
+ *     1 / d taken as 0 when d = 0 or when it overflows (|d| < 2^-128);
+ *     with f16 scales d is stored rounded to
+ *     f16 while the nibbles use the float32 d.  (The page's least-squares
+ *     Q4_0 search is not provided.)
+ * image (device, 16-byte aligned, at least min_span bytes) receives the
+ * bytes; they can be written to a file or uploaded with qmv_upload.
+ * status (a device uint32, 4-byte aligned) is set to 0, and to 1 if some
+ * f16 scale is above 65504 and cannot be stored (the image is then not a
+ * valid file's); read it once the work on `stream` is done.  Like the
+ * compute calls it only enqueues kernels (no allocation, no memset), so it
+ * can be captured in a graph.
+ * Errors: QMV_E_FORMAT (wtype, scale_f16), QMV_E_SHAPE, QMV_E_ARG (null or
+ * misaligned pointer, image too small), QMV_E_DEVICE.
+ */
+int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
+                         const float *w, void *image, uint64_t image_bytes, uint32_t *status,
+                         void *stream);
 
 /*
  * Per-block integer dot products of the weight quants with quantized

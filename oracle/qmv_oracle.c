@@ -406,7 +406,8 @@ int orc_gguf_to_image(uint32_t wtype, uint64_t rows, uint64_t cols,
  *     scales d is stored rounded to f16.
  * Readings (the page leaves these open): the element of largest magnitude
  * is the first one reaching it; a Q4_0 block with d = 0 uses 1 / d = 0
- * (every nibble 8, every weight 0), as llama.cpp does; the Q4_0 levels use
+ * (every nibble 8, every weight 0), as llama.cpp does, and so does one whose
+ * 1 / d overflows (|d| < 2^-128, weights below 2^-125); the Q4_0 levels use
  * the float32 d also when the stored scale is its f16 rounding (only the
  * Q8_0 sentence says "against that rounded d"); an f16 Q8_0 scale that
  * rounds to 0 from amax >= 1e-30 gives q = 0 (every weight is 0 either
@@ -511,6 +512,7 @@ int orc_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint64_t rows,
             }
             float d = mx / -8.0f;
             float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+            if (isinf(id)) id = 0.0f; /* |d| < 2^-128: the block writes as zeros */
             uint8_t *qb = img + 16 * k;
             for (int j = 0; j < 16; ++j) {
                 volatile float t0 = x[j] * id, t1 = x[j + 16] * id;

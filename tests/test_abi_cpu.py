@@ -25,7 +25,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     declared = header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 15
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -145,3 +145,61 @@ def test_oracle_and_product_share_no_code():
     for f in ("qmv_oracle.c", "__init__.py"):
         for ref in code_refs(os.path.join(ROOT, "oracle", f)):
             assert "block_quant_weight_amd" not in ref and "qmv.h" not in ref, (f, ref)
+
+
+def test_gguf_span_matches_oracle_and_page():
+    for wt in (1, 2):
+        for R, C in [(1, 32), (7, 96), (151936, 896), (248320, 1024), (16777216, 32)]:
+            st, n = O.gguf_span(wt, R, C)
+            assert Q.qmv_gguf_span(wt, R, C) == n
+    # the minfer page's byte counts (section 3.2 (g))
+    assert Q.qmv_gguf_span(1, 151936, 896) == 144_643_072
+    assert Q.qmv_gguf_span(2, 151936, 896) == 76_575_744
+    for args in [(3, 1, 32), (1, 1, 48), (1, 0, 32), (2, 16777217, 32)]:
+        st, _ = O.gguf_span(*args)
+        with pytest.raises(Q.QmvError) as e:
+            Q.qmv_gguf_span(*args)
+        assert e.value.status == CODES[st]
+    assert Q.lib().qmv_gguf_span(1, 1, 32, None) == Q.QMV_E_ARG
+
+
+def test_gguf_upload_host_checks():
+    # rejected on the host, before any device call: f32-scale handle, short
+    # data, a -128 quant (on this CPU-only machine a handle can be created but
+    # not uploaded, so only the refusals are checked here)
+    L = Q.lib()
+    R, C = 2, 64
+    blob = np.zeros(Q.qmv_gguf_span(1, R, C), dtype=np.uint8)
+    ptr = blob.ctypes.data_as(ctypes.c_void_p)
+    h32 = Q.qmv_create(1, 0, R, C)
+    try:
+        assert L.qmv_upload_gguf(h32.ptr, ptr, blob.size, None) == Q.QMV_E_FORMAT
+    finally:
+        Q.qmv_destroy(h32)
+    h = Q.qmv_create(1, 1, R, C)
+    try:
+        assert L.qmv_upload_gguf(h.ptr, ptr, blob.size - 1, None) == Q.QMV_E_FORMAT
+        bad = blob.copy()
+        bad[34 * 3 + 2 + 7] = 0x80
+        assert O.check_gguf(1, R, C, bad) == "format"
+        assert L.qmv_upload_gguf(h.ptr, bad.ctypes.data_as(ctypes.c_void_p), bad.size,
+                                 None) == Q.QMV_E_FORMAT
+        assert L.qmv_upload_gguf(h.ptr, None, 0, None) == Q.QMV_E_ARG
+    finally:
+        Q.qmv_destroy(h)
+
+
+def test_quantize_weights_host_checks():
+    L = Q.lib()
+    p = ctypes.c_void_p(4096)
+    assert L.qmv_quantize_weights(3, 0, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
+    assert L.qmv_quantize_weights(1, 2, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
+    assert L.qmv_quantize_weights(1, 0, 1, 48, p, p, 1 << 20, p, None) == Q.QMV_E_SHAPE
+    assert L.qmv_quantize_weights(1, 0, 1, 32, None, p, 1 << 20, p, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 0, 1, 32, p, p, 1 << 20, None, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 0, 1, 32, ctypes.c_void_p(4100), p, 1 << 20, p,
+                                  None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 0, 1, 32, p, p, 1 << 20, ctypes.c_void_p(4098),
+                                  None) == Q.QMV_E_ARG
+    need = Q.qmv_span(1, 1, 1, 32)["min_span"]
+    assert L.qmv_quantize_weights(1, 1, 1, 32, p, p, need - 1, p, None) == Q.QMV_E_ARG

@@ -182,6 +182,11 @@ def test_q4_round_writer_exact_recovery():
             # the largest magnitude is -8c, so d = c (negative when c is) and
             # x / d = k in both cases
             assert d.tolist() == [0.375 * sign] and nib.tolist() == (k + 8).tolist()
+    # a block so small that 1 / d overflows writes as zeros: nibbles 8
+    tiny = np.full(32, 1e-40, dtype=np.float32)
+    st, img = O.quantize_weights(Q4, 0, 1, 32, tiny)
+    q, d, _ = split_image(img, Q4, 0, 1, 32)
+    assert d.tolist() == [np.float32(1e-40) / np.float32(-8)] and set(q.tolist()) == {0x88}
     # an all-zero block: d = -0.0 (0 / -8), every nibble 8, every weight 0
     st, img = O.quantize_weights(Q4, 0, 1, 32, np.zeros(32, np.float32))
     q, d, _ = split_image(img, Q4, 0, 1, 32)
