@@ -78,6 +78,10 @@ def lib():
         L.orc_f16_bits.restype = ctypes.c_uint16
         L.orc_quantize_weights.argtypes = [u32, u32, u64, u64, vp, vp]
         L.orc_quantize_weights.restype = i32
+        L.orc_ffn_act.argtypes = [ctypes.c_double, u32]
+        L.orc_ffn_act.restype = ctypes.c_double
+        L.orc_gated.argtypes = [vp, vp, u64, u32, vp]
+        L.orc_gated.restype = None
         _lib = L
     return _lib
 
@@ -217,6 +221,46 @@ def within_tolerance(y, ref, norm, rel: float = 2e-3):
     ok = not bool(bad.any())
     pos = norm > 0
     worst = float((err[pos] / norm[pos]).max()) if pos.any() else 0.0
+    return ok, worst
+
+
+# ---- gated feed-forward pair: act(W1 x) * (W3 x) ----
+
+ACT_SILU = 0
+ACT_GELU_TANH = 1
+# max |act'(a)| over all a: SiLU 1.0998 (a = 2.40), GELU-tanh 1.1290 (a = 1.50)
+ACT_LIPSCHITZ = 1.13
+
+
+def ffn_act(a: float, act: int) -> float:
+    return float(lib().orc_ffn_act(float(a), act))
+
+
+def gated(img1, img3, wtype, scale_f16, rows, cols, x, act, sel=None, threads: int = 1):
+    """(h, y1, n1, y3, n3), each float64 [batch][len(sel)]: the two products
+    with their norms, and h = act(y1) * y3."""
+    y1, n1 = product(img1, wtype, scale_f16, rows, cols, x, sel, threads)
+    y3, n3 = product(img3, wtype, scale_f16, rows, cols, x, sel, threads)
+    h = np.zeros_like(y1)
+    lib().orc_gated(_ptr(y1), _ptr(y3), y1.size, act, _ptr(h))
+    return h, y1, n1, y3, n3
+
+
+def gated_within_tolerance(h, href, y1, n1, y3, n3, act, rel: float = 2e-3):
+    """Parity predicate on a gated output, propagated from the products'
+    bound e = rel * norm: |h - href| <= L e1 (|y3| + e3) + |act(y1)| e3 plus
+    2^-20 of (|act(y1)| + L e1)(|y3| + e3) for the float32 activation and
+    multiply, with L = max |act'|.  Returns (ok, worst ratio err / bound)."""
+    h = np.asarray(h, dtype=np.float64)
+    e1, e3 = rel * n1, rel * n3
+    a1 = np.abs(np.vectorize(lambda v: ffn_act(v, act))(y1)) if y1.size else y1
+    L = ACT_LIPSCHITZ
+    bound = L * e1 * (np.abs(y3) + e3) + a1 * e3
+    bound = bound + 2.0 ** -20 * (a1 + L * e1) * (np.abs(y3) + e3)
+    err = np.abs(h - href)
+    ok = bool((err <= bound).all())
+    pos = bound > 0
+    worst = float((err[pos] / bound[pos]).max()) if pos.any() else 0.0
     return ok, worst
 
 

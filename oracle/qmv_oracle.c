@@ -227,6 +227,32 @@ void orc_product(const uint8_t *img, uint32_t wtype, uint32_t scale_f16,
 }
 
 /*
+ * Feed-forward activation of the .mlb header field "act" (0 = SiLU, 1 = GELU
+ * with the tanh approximation, the Gemma convention), in binary64:
+ *   SiLU(a) = a / (1 + e^-a)   (a times the logistic sigmoid);
+ *   GELU(a) = a/2 * (1 + tanh(u)),  u = sqrt(2/pi) * (a + 0.044715 a^3)
+ *             (Hendrycks and Gimpel's tanh approximation of a * Phi(a)),
+ *             written as a / (1 + e^(-2u)): the same function, because
+ *             1 + tanh(u) = 2 / (1 + e^(-2u)), without the cancellation of
+ *             1 + tanh(u) that leaves no correct digit even in binary64 once
+ *             u < -19.
+ * The gated hidden state of a layer is act(w1 . x) * (w3 . x): w1 is the
+ * gate and w3 the up projection in the page's body table.
+ */
+double orc_ffn_act(double a, uint32_t act) {
+    if (act == 0) return a / (1.0 + exp(-a));
+    const double k = sqrt(2.0 / 3.14159265358979323846);
+    const double u = k * (a + 0.044715 * a * a * a);
+    return a / (1.0 + exp(-2.0 * u));
+}
+
+/* h[i] = act(y1[i]) * y3[i] for n elements (the gated output from the two
+ * products of orc_product). */
+void orc_gated(const double *y1, const double *y3, uint64_t n, uint32_t act, double *h) {
+    for (uint64_t i = 0; i < n; ++i) h[i] = orc_ffn_act(y1[i], act) * y3[i];
+}
+
+/*
  * Activation quantizer ("Quantization rule"), per block of 32, in float32
  * operations in the page's order:
  *   amax = max |x|;  amax < 1e-30 -> d = 0, q = 0;

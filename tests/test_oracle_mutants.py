@@ -142,3 +142,39 @@ def test_planted_writer_or_gguf_mistake_is_caught(tmp_path, monkeypatch, name, o
         except Exception:  # noqa: BLE001 - any failure of a pin counts
             failed.append(fn.__name__)
     assert failed, f"no pin catches: {name}"
+
+
+# ---- the gated feed-forward output ------------------------------------------
+
+import test_oracle_gated as G  # noqa: E402
+
+MUTANTS_G = [
+    ("SiLU with e^+a", "return a / (1.0 + exp(-a));", "return a / (1.0 + exp(a));"),
+    ("GELU cubic coefficient", "0.044715 * a * a * a", "0.44715 * a * a * a"),
+    ("GELU with e^-u", "return a / (1.0 + exp(-2.0 * u));", "return a / (1.0 + exp(-u));"),
+    ("GELU constant 2/pi", "sqrt(2.0 / 3.14159265358979323846)", "(2.0 / 3.14159265358979323846)"),
+    ("gate taken from the up projection", "orc_ffn_act(y1[i], act) * y3[i]",
+     "orc_ffn_act(y3[i], act) * y1[i]"),
+]
+
+
+def _pins_g():
+    out = [(G.test_silu_library_closed_form_and_identity, ()),
+           (G.test_gelu_tanh_near_exact_gelu_and_identity, ())]
+    for act in (0, 1):
+        out.append((G.test_lipschitz_constant_of_the_tolerance, (act,)))
+        for wt, sf in ((2, 1), (1, 1)):
+            out.append((G.test_gated_against_numpy_products, (act, wt, sf)))
+    return out
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_G, ids=[m[0] for m in MUTANTS_G])
+def test_planted_gated_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    _install(tmp_path, monkeypatch, old, new)
+    failed = []
+    for fn, args in _pins_g():
+        try:
+            fn(*args)
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(fn.__name__)
+    assert failed, f"no pin catches: {name}"
