@@ -11,7 +11,9 @@ bracketed by device synchronisation and HIP events on the launching stream.
 
 Default workload: Q4_0 GEMV, 4096 x 4096, f16 scales, batch 1.  Other
 workloads (--workload): q8_gemv_512, decode_layer (wq|wk|wv and w1|w3 grouped
-on their shared inputs), decode_layer_7 (one launch per matrix), gemm_q4_14336x4096,
+on their shared inputs), decode_layer_gated (the same, with w1|w3 as one gated
+launch, SiLU(w1 x) * (w3 x), whose output is w2's input), decode_layer_7 (one
+launch per matrix), gemm_q4_14336x4096,
 gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, writer_q4_14336x4096
 (the weight writer: float32 weights to a Q4_0 f16-scale image by the round
 rule), and copy (a plain device copy, used to calibrate HBM byte counters).
@@ -54,12 +56,14 @@ def workload(name):
     if name == "q8_gemv_512":
         return ("Q8_0 GEMV 512x512, f32 scales, batch 1", "gemv", 1,
                 [(0, Q8, 0, 512, 512)], 1)
-    if name in ("decode_layer", "decode_layer_7"):
+    if name in ("decode_layer", "decode_layer_7", "decode_layer_gated"):
         mats = []
         for m, (_, cls, r, c) in enumerate(LAYER):
             mats.append((m, Q.qmv_class_wtype(Q4, 8 | 64, cls, 0), 1, r, c))
-        how = ("4 launches: wq|wk|wv and w1|w3 grouped on their shared inputs"
-               if name == "decode_layer" else "7 launches, one per matrix")
+        how = {"decode_layer": "4 launches: wq|wk|wv and w1|w3 grouped on their shared inputs",
+               "decode_layer_gated": "4 launches: wq|wk|wv grouped, w1|w3 as one gated "
+                                     "launch h = SiLU(w1 x) * (w3 x), w2 on h",
+               "decode_layer_7": "7 launches, one per matrix"}[name]
         return ("mixed decode layer (q8_mask 8|64: wv, w2 Q8_0; others Q4_0), "
                 f"dim 4096, kv 1024, ffn 11008, f16 scales, batch 1, {how}", "gemv", 3, mats, 1)
     if name == "gemm_q4_14336x4096":
@@ -85,6 +89,8 @@ def workload(name):
 
 # launches of the fused decode layer: indexes into LAYER (shared activations)
 LAYER_GROUPS = [(0, 1, 2), (3,), (4, 5), (6,)]
+# the gated pair (w1, w3) and the matrix that takes its output (w2)
+GATED_PAIR, GATED_NEXT = (4, 5), 6
 
 # The kernel that the library's dispatch runs for each workload's largest
 # launch (the roofline's kernel), and the source file it is built from.
@@ -92,6 +98,7 @@ DOMINANT_KERNEL = {
     "q4_gemv_4096": ("gemv_oneshot_kernel", "gemv.hip"),
     "q8_gemv_512": ("gemv_oneshot_kernel", "gemv.hip"),
     "decode_layer": ("gemv_stream_kernel (w1|w3)", "gemv.hip"),
+    "decode_layer_gated": ("gemv_stream_kernel, gated (w1|w3)", "gemv.hip"),
     "decode_layer_7": ("gemv_oneshot_kernel (w2)", "gemv.hip"),
     "lm_head_b1": ("gemv_oneshot_kernel", "gemv.hip"),
     "lm_head_b64": ("gemv_mfma_kernel (f16 operands)", "gemv_mfma.hip"),
@@ -104,7 +111,7 @@ DOMINANT_KERNEL = {
 
 def launch_groups(name, mats):
     """Lists of matrix positions that share one launch and one x."""
-    if name == "decode_layer":
+    if name in ("decode_layer", "decode_layer_gated"):
         return [list(g) for g in LAYER_GROUPS]
     return [[i] for i in range(len(mats))]
 
@@ -114,13 +121,16 @@ def matrix_bytes(wt, sf, r, c):
     return q + (r * c // 32) * (2 if sf else 4)
 
 
-def step_work(kind, mats, batch, groups=None):
+def step_work(kind, mats, batch, groups=None, gated=False):
     """Algorithmic bytes and flops of one step (an activation vector shared
-    by a launch group is counted once)."""
+    by a launch group is counted once; with gated, the group of two writes
+    one output vector, act(y1) * y3)."""
     byts = flops = 0
     if kind == "gemv" and groups is not None:
         for g in groups:
             byts += 4 * mats[g[0]][4] * batch
+            if gated and len(g) == 2:
+                byts -= 4 * mats[g[1]][3] * batch
         for _, wt, sf, r, c in mats:
             byts += matrix_bytes(wt, sf, r, c) + 4 * r * batch
             flops += 2 * r * c * batch
@@ -298,7 +308,9 @@ def main():
         return
 
     groups = launch_groups(args.workload, mats)
-    step_bytes, step_flops = step_work(kind, mats, batch, groups if kind == "gemv" else None)
+    gated = args.workload == "decode_layer_gated"
+    step_bytes, step_flops = step_work(kind, mats, batch, groups if kind == "gemv" else None,
+                                       gated)
     set_bytes = sum(matrix_bytes(wt, sf, r, c) for _, wt, sf, r, c in mats)
     ncopies = max(2, -(-ROTATE_BYTES // set_bytes))
     if kind == "embed":
@@ -341,14 +353,21 @@ def main():
             id_sets.append(torch.from_numpy(ids).cuda())
         out = torch.empty((batch, mats[0][4]), dtype=torch.float32, device="cuda")
 
+    def run_group(hs, gr):
+        if gated and tuple(gr) == GATED_PAIR:
+            Q.qmv_gemv_gated(hs[gr[0]], hs[gr[1]], xs[gr[0]], ys[gr[0]], act=Q.ACT_SILU)
+        elif gated and gr[0] == GATED_NEXT:
+            Q.qmv_gemv(hs[gr[0]], ys[GATED_PAIR[0]], ys[gr[0]])
+        elif len(gr) == 1:
+            Q.qmv_gemv(hs[gr[0]], xs[gr[0]], ys[gr[0]])
+        else:
+            Q.qmv_gemv_group([hs[j] for j in gr], xs[gr[0]], [ys[j] for j in gr])
+
     def step(i):
         hs = handles[i % ncopies]
         if kind == "gemv":
             for gr in groups:
-                if len(gr) == 1:
-                    Q.qmv_gemv(hs[gr[0]], xs[gr[0]], ys[gr[0]])
-                else:
-                    Q.qmv_gemv_group([hs[j] for j in gr], xs[gr[0]], [ys[j] for j in gr])
+                run_group(hs, gr)
             return
         for j, h in enumerate(hs):
             if kind == "gemv":
@@ -400,7 +419,8 @@ def main():
         dom = max(range(len(groups)),
                   key=lambda k: sum(matrix_bytes(*mats[j][1:]) for j in groups[k]))
         gr = groups[dom]
-        dom_bytes, _ = step_work(kind, [mats[j] for j in gr], batch, [list(range(len(gr)))])
+        dom_bytes, _ = step_work(kind, [mats[j] for j in gr], batch, [list(range(len(gr)))],
+                                 gated)
         # this launch rotates over its own >= 512 MB of copies: the step's
         # copies plus extra uploads of the group's matrices
         dom_set = sum(matrix_bytes(*mats[j][1:]) for j in gr)
@@ -418,11 +438,7 @@ def main():
             dom_handles.append(hs)
 
         def launch(i):
-            hs = dom_handles[i % dom_copies]
-            if len(gr) == 1:
-                Q.qmv_gemv(hs[gr[0]], xs[gr[0]], ys[gr[0]])
-            else:
-                Q.qmv_gemv_group([hs[j] for j in gr], xs[gr[0]], [ys[j] for j in gr])
+            run_group(dom_handles[i % dom_copies], gr)
         for i in range(warmup):
             launch(i)
         torch.cuda.synchronize()

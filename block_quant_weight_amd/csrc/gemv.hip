@@ -677,11 +677,73 @@ __device__ __forceinline__ void load_tile(const TileArgs& g, uint32_t t, uint32_
     b.wrows = wrows;
 }
 
+// Gated tile t: rows [t * NR/2, t * NR/2 + NR/2) of w1 (g.q[0], g.d[0]) in
+// register rows 0 .. NR/2 - 1 and the same rows of w3 (g.q[1], g.d[1]) in
+// rows NR/2 .. NR - 1; b.wrows counts the rows of one matrix.
+template <uint32_t WT, bool SF16, int NR, int SMAX>
+__device__ __forceinline__ void load_tile_gated(const TileArgs& g, uint32_t t, uint32_t cols,
+                                                uint32_t lane, TileRegs<NR, SMAX>& b) {
+    constexpr int NH = NR / 2;
+    constexpr uint32_t CW = DigitLayout<WT>::CW;
+    constexpr uint32_t SB = SF16 ? 2 : 4;
+    const bool live = t < g.first[1];
+    const uint32_t rows = g.rows[0];
+    const uint32_t row0 = live ? t * NH : 0;
+    const uint32_t wrows = live ? min(static_cast<uint32_t>(NH), rows - row0) : 0;
+    const uint32_t nchunks = cols / CW;
+    const uint64_t row_bytes = (WT == kQ4) ? (cols >> 1) : cols;
+    const uint32_t nblk = cols >> 5;
+    __amdgpu_buffer_rsrc_t qrs[2], drs[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        qrs[m] = make_rsrc(g.q[m] + static_cast<uint64_t>(row0) * row_bytes,
+                           wrows * static_cast<uint32_t>(row_bytes));
+        drs[m] = make_rsrc(static_cast<const uint8_t*>(g.d[m]) + static_cast<uint64_t>(row0) * nblk * SB,
+                           wrows * nblk * SB);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const uint32_t ch = lane + 64 * k;
+            const uint32_t blk = (WT == kQ4) ? ch : (ch >> 1);
+            const uint32_t dofs = ch < nchunks ? ((r % NH) * nblk + blk) * SB : kOob;
+            if constexpr (SF16) b.d[r][k] = __builtin_amdgcn_raw_buffer_load_b16(drs[r / NH], dofs, 0, 0);
+            else b.d[r][k] = __builtin_amdgcn_raw_buffer_load_b32(drs[r / NH], dofs, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+#pragma unroll
+        for (int k = 0; k < SMAX; ++k) {
+            const uint32_t ch = lane + 64 * k;
+            const uint32_t qo = ch < nchunks ? (r % NH) * static_cast<uint32_t>(row_bytes) + 16 * ch : kOob;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qrs[r / NH], qo, 0, 0);
+            b.q[r][k] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    }
+    b.mat = 0;
+    b.row0 = row0;
+    b.wrows = wrows;
+}
+
+// The FFN activations of the .mlb header field `act`: 0 SiLU, a * sigmoid(a);
+// 1 GELU with the tanh approximation, a/2 * (1 + tanh(u)) with u =
+// sqrt(2/pi) * (a + 0.044715 a^3), evaluated as a / (1 + e^(-2u)) (the same
+// function, since 1 + tanh(u) = 2 / (1 + e^(-2u))): 1 + tanh(u) would lose
+// all relative precision to cancellation for negative a.
+__device__ __forceinline__ float ffn_act(float a, uint32_t act) {
+    if (act == 0) return a / (1.0f + expf(-a));
+    const float u = 0.7978845608028654f * (a + 0.044715f * a * a * a);
+    return a / (1.0f + expf(-2.0f * u));
+}
+
 // Multiplies a loaded tile by the NB staged vectors and stores its rows.
-template <uint32_t WT, bool SF16, int NR, int NB, int SMAX>
+// Gated (GATED = true): stores act(w1 row) * (w3 row) for each row pair.
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED>
 __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<NR, SMAX>& b,
                                              const uint8_t* __restrict__ lds, uint32_t cols,
-                                             uint32_t S, uint32_t lane) {
+                                             uint32_t S, uint32_t lane, uint32_t act) {
     using L = DigitLayout<WT>;
     constexpr int P = L::P;
     const uint32_t nchunks = cols / L::CW;
@@ -726,19 +788,32 @@ __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<N
     }
     const uint32_t rows = g.rows[b.mat];
     float* y = g.y[b.mat];
+    if constexpr (GATED) {
+        constexpr int NH = NR / 2;
 #pragma unroll
-    for (int v = 0; v < NB; ++v)
+        for (int v = 0; v < NB; ++v)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float sum = wave_reduce(acc[v][r]);
-            if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
-                y[static_cast<uint64_t>(v) * rows + b.row0 + r] = sum;
-        }
+            for (int r = 0; r < NH; ++r) {
+                const float s1 = wave_reduce(acc[v][r]);
+                const float s3 = wave_reduce(acc[v][r + NH]);
+                if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
+                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = ffn_act(s1, act) * s3;
+            }
+    } else {
+#pragma unroll
+        for (int v = 0; v < NB; ++v)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float sum = wave_reduce(acc[v][r]);
+                if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
+                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = sum;
+            }
+    }
 }
 
-template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int DEPTH>
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int DEPTH, bool GATED = false>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
-    TileArgs g, const float* __restrict__ x, uint32_t cols, uint32_t per_wg) {
+    TileArgs g, const float* __restrict__ x, uint32_t cols, uint32_t per_wg, uint32_t act) {
     extern __shared__ float4 smem[];
     using L = DigitLayout<WT>;
     constexpr int THREADS = kStreamWaves * 64;
@@ -782,8 +857,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     // tiles at or past `end` load nothing
     auto tile = [&](uint32_t u) { return u < end ? u : 0xFFFFFFFEu; };
     TileRegs<NR, SMAX> ra, rb, rc;
-    load_tile<WT, SF16, NR, SMAX>(g, tile(t), cols, lane, mat, ra);
-    if constexpr (DEPTH == 3) load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, rb);
+    auto load_any = [&](uint32_t u, TileRegs<NR, SMAX>& regs) {
+        if constexpr (GATED) load_tile_gated<WT, SF16, NR, SMAX>(g, u, cols, lane, regs);
+        else load_tile<WT, SF16, NR, SMAX>(g, u, cols, lane, mat, regs);
+    };
+    load_any(tile(t), ra);
+    if constexpr (DEPTH == 3) load_any(tile(t + step), rb);
 
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t v = j / nhalf, h = j - v * nhalf;
@@ -807,27 +886,27 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
         // three register sets in rotation: the loads of the next two tiles
         // are in flight while a tile is multiplied
         while (t < end) {
-            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, rc);
-            compute_tile<WT, SF16, NR, NB, SMAX>(g, ra, lds, cols, S, lane);
+            load_any(tile(t + 2 * step), rc);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, cols, S, lane, act);
             t += step;
             if (t >= end) break;
-            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, ra);
-            compute_tile<WT, SF16, NR, NB, SMAX>(g, rb, lds, cols, S, lane);
+            load_any(tile(t + 2 * step), ra);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, cols, S, lane, act);
             t += step;
             if (t >= end) break;
-            load_tile<WT, SF16, NR, SMAX>(g, tile(t + 2 * step), cols, lane, mat, rb);
-            compute_tile<WT, SF16, NR, NB, SMAX>(g, rc, lds, cols, S, lane);
+            load_any(tile(t + 2 * step), rb);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rc, lds, cols, S, lane, act);
             t += step;
         }
     } else {
         // two register sets: the next tile's loads are in flight
         while (t < end) {
-            load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, rb);
-            compute_tile<WT, SF16, NR, NB, SMAX>(g, ra, lds, cols, S, lane);
+            load_any(tile(t + step), rb);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, cols, S, lane, act);
             t += step;
             if (t >= end) break;
-            load_tile<WT, SF16, NR, SMAX>(g, tile(t + step), cols, lane, mat, ra);
-            compute_tile<WT, SF16, NR, NB, SMAX>(g, rb, lds, cols, S, lane);
+            load_any(tile(t + step), ra);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, cols, S, lane, act);
             t += step;
         }
     }
@@ -944,10 +1023,10 @@ hipError_t stream_launch(const MatView* ms, uint32_t n, const float* x, float* c
     const float* xp = x + static_cast<uint64_t>(done) * cols;
     if (tune_knob("QMV_STREAM_DEPTH", 2) == 3)
         hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 3>), dim3(blocks),
-                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg);
+                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
     else
         hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 2>), dim3(blocks),
-                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg);
+                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
     return hipGetLastError();
 }
 
@@ -1032,6 +1111,71 @@ hipError_t gemv_batched(const MatView& m, const float* x, float* y,
         else if (nb == 4) e = gemv_pass<WT, SF16, 4>(m, xp, yp, s);
         else if (nb == 2) e = gemv_pass<WT, SF16, 2>(m, xp, yp, s);
         else e = gemv_pass<WT, SF16, 1>(m, xp, yp, s);
+        if (e != hipSuccess) return e;
+        done += nb;
+    }
+    return hipSuccess;
+}
+
+// Gated launch over row pairs of w1 | w3 (one storage and scale type): NR/2
+// rows of each per tile, NB activation vectors, h = act(w1 x) * (w3 x).
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX>
+hipError_t gated_launch(const MatView& w1, const MatView& w3, uint32_t act, const float* x,
+                        float* h, uint32_t done, hipStream_t s) {
+    TileArgs g{};
+    g.n = 1;
+    g.q[0] = w1.q;
+    g.d[0] = w1.d;
+    g.q[1] = w3.q;
+    g.d[1] = w3.d;
+    g.y[0] = h + static_cast<uint64_t>(done) * w1.rows;
+    g.rows[0] = w1.rows;
+    const uint32_t tiles = (w1.rows + NR / 2 - 1) / (NR / 2);
+    g.first[0] = 0;
+    g.first[1] = tiles;
+    for (uint32_t i = 2; i <= static_cast<uint32_t>(kMaxGroup); ++i) g.first[i] = 0x7FFFFFFFu;
+    const uint32_t cols = w1.cols;
+    const uint32_t want = (tiles + kStreamWaves - 1) / kStreamWaves;
+    const uint32_t blocks = want < 256 ? want : 256;
+    const uint32_t per_wg = (tiles + blocks - 1) / blocks;
+    const size_t lds = static_cast<size_t>(gemv_lds_bytes<WT>(cols, NB));
+    const float* xp = x + static_cast<uint64_t>(done) * cols;
+    hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 2, true>), dim3(blocks),
+                       dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, act);
+    return hipGetLastError();
+}
+
+template <uint32_t WT, bool SF16, int NB>
+hipError_t gated_pass(const MatView& w1, const MatView& w3, uint32_t act, const float* x, float* h,
+                      uint32_t done, hipStream_t s) {
+    const uint32_t S = (w1.cols / DigitLayout<WT>::CW + 63) / 64;
+    if (S == 1) return gated_launch<WT, SF16, 4, NB, 1>(w1, w3, act, x, h, done, s);
+    if (S == 2) return gated_launch<WT, SF16, 2, NB, 2>(w1, w3, act, x, h, done, s);
+    // rows of 3 or 4 steps: one vector per pass (more would spill registers)
+    if constexpr (NB == 1) return gated_launch<WT, SF16, 2, 1, 4>(w1, w3, act, x, h, done, s);
+    return hipErrorNotSupported;
+}
+
+// Vectors per gated pass: 4, 2 or 1, as many as are left and fit 64 KiB of
+// LDS; 1 for rows of more than two steps.
+template <uint32_t WT>
+uint32_t gated_vectors(uint32_t cols, uint32_t left) {
+    if ((cols / DigitLayout<WT>::CW + 63) / 64 > 2) return 1;
+    uint32_t nb = left >= 4 ? 4 : left >= 2 ? 2 : 1;
+    while (nb > 1 && gemv_lds_bytes<WT>(cols, nb) > kOneshotLds) nb /= 2;
+    return nb;
+}
+
+template <uint32_t WT, bool SF16>
+hipError_t gated_batched(const MatView& w1, const MatView& w3, uint32_t act, const float* x,
+                         float* h, uint32_t batch, hipStream_t s) {
+    uint32_t done = 0;
+    while (done < batch) {
+        const uint32_t nb = gated_vectors<WT>(w1.cols, batch - done);
+        hipError_t e;
+        if (nb == 4) e = gated_pass<WT, SF16, 4>(w1, w3, act, x, h, done, s);
+        else if (nb == 2) e = gated_pass<WT, SF16, 2>(w1, w3, act, x, h, done, s);
+        else e = gated_pass<WT, SF16, 1>(w1, w3, act, x, h, done, s);
         if (e != hipSuccess) return e;
         done += nb;
     }
@@ -1124,6 +1268,25 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
         done += nb;
     }
     return hipSuccess;
+}
+
+bool gemv_gated_fits(const MatView& w1, const MatView& w3) {
+    if (w1.wtype != w3.wtype || w1.scale_f16 != w3.scale_f16 || w1.rows != w3.rows ||
+        w1.cols != w3.cols)
+        return false;
+    const uint32_t cw = w1.wtype == kQ4 ? 32 : 16;
+    const uint64_t row_bytes = w1.wtype == kQ4 ? w1.cols / 2 : w1.cols;
+    return (w1.cols / cw + 63) / 64 <= 4 && 2 * row_bytes < 0xFFFFFFF0ull;
+}
+
+hipError_t launch_gemv_gated(const MatView& w1, const MatView& w3, uint32_t act, const float* x,
+                             float* h, uint32_t batch, hipStream_t s) {
+    if (!gemv_gated_fits(w1, w3) || act > 1) return hipErrorNotSupported;
+    if (w1.wtype == kQ4)
+        return w1.scale_f16 ? gated_batched<kQ4, true>(w1, w3, act, x, h, batch, s)
+                            : gated_batched<kQ4, false>(w1, w3, act, x, h, batch, s);
+    return w1.scale_f16 ? gated_batched<kQ8, true>(w1, w3, act, x, h, batch, s)
+                        : gated_batched<kQ8, false>(w1, w3, act, x, h, batch, s);
 }
 
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,

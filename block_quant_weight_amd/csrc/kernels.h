@@ -23,6 +23,16 @@ hipError_t launch_gemv(const MatView& m, const float* x, float* y,
 hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, float* const* ys,
                              uint32_t batch, hipStream_t stream);
 
+// Gated pair of a feed-forward layer: h[t][r] = act(sum_c W1[r][c] x[t][c]) *
+// sum_c W3[r][c] x[t][c], act 0 = SiLU, 1 = GELU (tanh form), in one launch
+// per pass of up to 4 vectors.  gemv_gated_fits tells whether a pair can
+// (the same storage type, scale type and shape, rows of <= 4 steps of 64
+// chunks: cols <= 8192 for Q4_0, <= 4096 for Q8_0); otherwise
+// launch_gemv_gated returns hipErrorNotSupported.
+bool gemv_gated_fits(const MatView& w1, const MatView& w3);
+hipError_t launch_gemv_gated(const MatView& w1, const MatView& w3, uint32_t act, const float* x,
+                             float* h, uint32_t batch, hipStream_t stream);
+
 // Same product on the matrix cores: x is bf16 bits, or f32 split into two
 // bf16 terms (x_f32 = true).  Large batches may split K; the slices' partial
 // sums then go to `workspace` (gemm_workspace_bytes of them; ignored when

@@ -221,6 +221,22 @@ int qmv_gemv_group(const qmv_handle* hs, uint32_t n, const float* x, float* cons
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int qmv_gemv_gated(qmv_handle w1, qmv_handle w3, uint32_t act, const float* x, float* h,
+                   uint32_t batch, void* stream) {
+    int st = ready(w1);
+    if (st != QMV_OK) return st;
+    st = ready(w3);
+    if (st != QMV_OK) return st;
+    if (x == nullptr || h == nullptr || batch == 0 || act > 1) return QMV_E_ARG;
+    if (!aligned16(x) || !aligned16(h)) return QMV_E_ARG;
+    const qmv::MatView a = view(w1), b = view(w3);
+    if (a.rows != b.rows || a.cols != b.cols) return QMV_E_SHAPE;
+    if (a.wtype != b.wtype || a.scale_f16 != b.scale_f16) return QMV_E_FORMAT;
+    if (!qmv::gemv_gated_fits(a, b)) return QMV_E_SHAPE;
+    return device_status(qmv::launch_gemv_gated(a, b, act, x, h, batch,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
              void* stream) {
     int st = ready(h);

@@ -23,7 +23,7 @@ QMV_E_NOMEM = -5
 EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
-           "qmv_upload_gguf", "qmv_quantize_weights")
+           "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated")
 
 _lib = None
 
@@ -59,6 +59,7 @@ def lib():
             "qmv_gguf_span": ([u32, u32, u32, pu64], i32),
             "qmv_upload_gguf": ([vp, vp, u64, vp], i32),
             "qmv_quantize_weights": ([u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
+            "qmv_gemv_gated": ([vp, vp, u32, vp, vp, u32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -223,6 +224,21 @@ def qmv_gemv_group(hs, x, ys, batch=None, stream=None):
     _check(lib().qmv_gemv_group(ctypes.cast(harr, ctypes.c_void_p), n, px,
                                 ctypes.cast(yarr, ctypes.c_void_p), b, _stream(stream)),
            "qmv_gemv_group")
+
+
+ACT_SILU = 0
+ACT_GELU_TANH = 1
+
+
+def qmv_gemv_gated(w1: QmvHandle, w3: QmvHandle, x, h, act=ACT_SILU, batch=None, stream=None):
+    """h = act(W1 x) * (W3 x) per row; x: float32 [batch, cols] on the GPU,
+    h: float32 [batch, rows]; act 0 = SiLU, 1 = GELU (tanh form)."""
+    import torch
+    b = x.shape[0] if (batch is None and x.dim() == 2) else (batch or 1)
+    px = _dev(x, torch.float32, b * w1.cols, "x")
+    ph = _dev(h, torch.float32, b * w1.rows, "h")
+    _check(lib().qmv_gemv_gated(w1.ptr, w3.ptr, act, px, ph, b, _stream(stream)),
+           "qmv_gemv_gated")
 
 
 def qmv_gemm(h: QmvHandle, x_bf16, y, batch=None, stream=None):

@@ -196,6 +196,27 @@ int qmv_gemv_group(const qmv_handle *hs, uint32_t n, const float *x,
                    float *const *ys, uint32_t batch, void *stream);
 
 /*
+ * Gated feed-forward pair of a decode layer in one launch:
+ *   h[t][r] = act(sum_c W1[r][c] x[t][c]) * sum_c W3[r][c] x[t][c],
+ * w1 the gate and w3 the up projection (the .mlb page's body table), act
+ * the header field of that name: 0 = SiLU, a / (1 + e^-a); 1 = GELU with
+ * the tanh approximation, a/2 (1 + tanh(sqrt(2/pi) (a + 0.044715 a^3))).
+ * Both sums are the products qmv_gemv computes (the same per-row
+ * arithmetic); the activation is the device's float32 expf / tanhf, and
+ * the row pair is multiplied once, so h is within the propagated bound
+ * (|act'| <= 1.13) of the exact result plus a few float32 rounding steps.
+ * x: float32 [batch][cols], h: float32 [batch][rows], device memory,
+ * 16-byte aligned; batch passes of up to 4 vectors.
+ * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, act > 1, a handle
+ * not uploaded), QMV_E_SHAPE (rows or cols differ, or rows longer than four
+ * steps: cols > 8192 for Q4_0, > 4096 for Q8_0 — such a pair runs as
+ * qmv_gemv_group and the caller's activation), QMV_E_FORMAT (the two differ
+ * in storage or scale type), QMV_E_DEVICE.
+ */
+int qmv_gemv_gated(qmv_handle w1, qmv_handle w3, uint32_t act, const float *x,
+                   float *h, uint32_t batch, void *stream);
+
+/*
  * Prefill product (GEMM), y[t][r] = sum_c W[r][c] * x[t][c], with x given
  * as bfloat16 bit patterns: x_bf16 uint16 [batch][cols], y float32
  * [batch][rows], device memory.  Tiles of W are decoded to bfloat16
