@@ -78,6 +78,8 @@ def lib():
         L.orc_f16_bits.restype = ctypes.c_uint16
         L.orc_quantize_weights.argtypes = [u32, u32, u64, u64, vp, vp]
         L.orc_quantize_weights.restype = i32
+        L.orc_quantize_q4_search.argtypes = [u32, u64, u64, vp, vp]
+        L.orc_quantize_q4_search.restype = i32
         L.orc_ffn_act.argtypes = [ctypes.c_double, u32]
         L.orc_ffn_act.restype = ctypes.c_double
         L.orc_gated.argtypes = [vp, vp, u64, u32, vp]
@@ -314,4 +316,18 @@ def quantize_weights(wtype, scale_f16, rows, cols, w: np.ndarray):
         raise ValueError("w has the wrong size")
     img = np.zeros(s["full_span"], dtype=np.uint8)
     st = lib().orc_quantize_weights(wtype, scale_f16, rows, cols, _ptr(wf), _ptr(img))
+    return OUTCOME[st], (img if st == 0 else None)
+
+
+def quantize_q4_search(scale_f16, rows, cols, w: np.ndarray):
+    """(outcome, image): Q4_0 by the least-squares search (13 candidate
+    levels, weights x^2); outcome 'format' for a refused block."""
+    st, s = span(Q4_0, scale_f16, rows, cols)
+    if st != "ok":
+        return st, None
+    wf = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    if wf.size != rows * cols:
+        raise ValueError("w has the wrong size")
+    img = np.zeros(s["full_span"], dtype=np.uint8)
+    st = lib().orc_quantize_q4_search(scale_f16, rows, cols, _ptr(wf), _ptr(img))
     return OUTCOME[st], (img if st == 0 else None)

@@ -439,7 +439,7 @@ int orc_gguf_to_image(uint32_t wtype, uint64_t rows, uint64_t cols,
  * rounds to 0 from amax >= 1e-30 gives q = 0 (every weight is 0 either
  * way); the f16 rounding is the oracle's own round-to-nearest-even of the
  * float32 value; a Q4_0 f16 scale above 65504 is refused like a Q8_0 one.
- * The least-squares Q4_0 search is not written.
+ * The least-squares Q4_0 search is orc_quantize_q4_search below.
  * Returns ORC_OK, ORC_SHAPE / ORC_FORMAT as orc_span, or ORC_FORMAT for a
  * scale that does not fit f16 (then img is unspecified).  img receives
  * full_span bytes (both pads zero).
@@ -558,6 +558,110 @@ int orc_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint64_t rows,
             dptr[2 * k + 1] = (uint8_t)(dbits16 >> 8);
         } else {
             memcpy(dptr + 4 * k, &dstore, 4);
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Q4_0 least-squares search (the .mlb page's paragraph on the Q4_0 writer
+ * that fits each block, the page's default), per block of 32 weights x:
+ *   1. the element of largest magnitude mx (the first to reach amax);
+ *      amax = 0 writes d = 0 and nibbles 8;
+ *   2. a block with amax < 1e-6 is divided by amax (its largest magnitude
+ *      becomes exactly 1) and its fitted d multiplied back by amax;
+ *   3. for each candidate level L = -6.0, -6.2, ..., -8.4 (13 values, the
+ *      float32 nearest each decimal): iscale = L / mx, level
+ *      l = rint(x * iscale) clamped to [-8, 7], then the weighted
+ *      least-squares scale with weights w = x^2,
+ *        d = sum w x l / sum w l^2,
+ *      and its weighted error  E = sum w (x - d l)^2;
+ *   4. the candidate with the smallest E wins (the first on ties; a NaN E
+ *      never replaces an earlier candidate);
+ *   5. nibbles = l + 8 of the winner; with f16 scales d is rounded to the
+ *      nearest f16 (the nibbles stay those of the fit).
+ * Readings (the page leaves these open): float32 throughout, each
+ * operation rounded on its own (no fused multiply-add), the sums taken in
+ * element order j = 0..31 with terms (w x) l, w (l l) and w (r r),
+ * r = x - d l; rint rounds half to even (the usual numpy rounding); a fit
+ * that is not finite (cubes overflow float32 once amax is above about 2^42)
+ * and an f16 scale above 65504 are refused.
+ * Returns ORC_OK, ORC_SHAPE / ORC_FORMAT as orc_span, or ORC_FORMAT for a
+ * refused block (img then unspecified).  img receives full_span bytes.
+ * ---------------------------------------------------------------------- */
+static const float ORC_LSQ_LEVEL[13] = {-6.0f, -6.2f, -6.4f, -6.6f, -6.8f, -7.0f, -7.2f,
+                                        -7.4f, -7.6f, -7.8f, -8.0f, -8.2f, -8.4f};
+
+/* levels of candidate L for the (scaled) block v with largest element mx */
+static void orc_lsq_levels(const float *v, float mx, float L, float *l) {
+    float iscale = L / mx;
+    for (int j = 0; j < 32; ++j) {
+        float t = rintf(v[j] * iscale);
+        if (t < -8.0f) t = -8.0f;
+        if (t > 7.0f) t = 7.0f;
+        l[j] = t;
+    }
+}
+
+int orc_quantize_q4_search(uint32_t scale_f16, uint64_t rows, uint64_t cols,
+                           const float *w, uint8_t *img) {
+    uint64_t span[5];
+    int st = orc_span(ORC_Q4_0, scale_f16, rows, cols, span);
+    if (st != ORC_OK) return st;
+    memset(img, 0, span[4]);
+    uint64_t nblk = rows * (cols / 32);
+    uint8_t *dptr = img + span[1];
+    for (uint64_t k = 0; k < nblk; ++k) {
+        const float *x = w + 32 * k;
+        float amax = 0.0f, mx = 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            float a = fabsf(x[j]);
+            if (a > amax) { amax = a; mx = x[j]; }
+        }
+        float d = 0.0f, best_l[32];
+        for (int j = 0; j < 32; ++j) best_l[j] = 0.0f;
+        if (amax != 0.0f) {
+            float v[32], wt[32], cube[32], l[32];
+            const int tiny = amax < 1e-6f;
+            for (int j = 0; j < 32; ++j) v[j] = tiny ? x[j] / amax : x[j];
+            float m = tiny ? mx / amax : mx;
+            for (int j = 0; j < 32; ++j) {
+                wt[j] = v[j] * v[j];
+                cube[j] = wt[j] * v[j];
+            }
+            float best_e = 0.0f;
+            for (int i = 0; i < 13; ++i) {
+                orc_lsq_levels(v, m, ORC_LSQ_LEVEL[i], l);
+                float sxl = 0.0f, sll = 0.0f;
+                for (int j = 0; j < 32; ++j) {
+                    sxl += cube[j] * l[j];
+                    sll += wt[j] * (l[j] * l[j]);
+                }
+                float dc = sxl / sll;
+                float e = 0.0f;
+                for (int j = 0; j < 32; ++j) {
+                    float r = v[j] - dc * l[j];
+                    e += wt[j] * (r * r);
+                }
+                if (i == 0 || e < best_e) {
+                    best_e = e;
+                    d = dc;
+                    memcpy(best_l, l, sizeof best_l);
+                }
+            }
+            if (tiny) d = d * amax;
+            if (!isfinite(d)) return ORC_FORMAT;
+        }
+        uint8_t *qb = img + 16 * k;
+        for (int j = 0; j < 16; ++j)
+            qb[j] = (uint8_t)((unsigned)(best_l[j] + 8.0f) | ((unsigned)(best_l[j + 16] + 8.0f) << 4));
+        if (scale_f16) {
+            uint16_t b = orc_f16_bits(d);
+            if ((b & 0x7FFFu) >= 0x7C00u) return ORC_FORMAT; /* > 65504 */
+            dptr[2 * k] = (uint8_t)(b & 0xFFu);
+            dptr[2 * k + 1] = (uint8_t)(b >> 8);
+        } else {
+            memcpy(dptr + 4 * k, &d, 4);
         }
     }
     return ORC_OK;

@@ -178,3 +178,41 @@ def test_planted_gated_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
         except Exception:  # noqa: BLE001 - any failure of a pin counts
             failed.append(fn.__name__)
     assert failed, f"no pin catches: {name}"
+
+
+# ---- the Q4_0 least-squares writer ------------------------------------------
+
+import test_oracle_q4_search as S  # noqa: E402
+
+MUTANTS_S = [
+    ("candidate step 0.25", "-6.2f, -6.4f, -6.6f", "-6.25f, -6.4f, -6.6f"),
+    ("12 candidates", "for (int i = 0; i < 13; ++i) {\n                orc_lsq_levels",
+     "for (int i = 0; i < 12; ++i) {\n                orc_lsq_levels"),
+    ("weights |x| instead of x^2", "wt[j] = v[j] * v[j];", "wt[j] = fabsf(v[j]);"),
+    ("levels truncated", "float t = rintf(v[j] * iscale);", "float t = truncf(v[j] * iscale);"),
+    ("levels clamped to 8", "if (t > 7.0f) t = 7.0f;", "if (t > 8.0f) t = 8.0f;"),
+    ("tiny threshold 1e-7", "const int tiny = amax < 1e-6f;", "const int tiny = amax < 1e-7f;"),
+    ("tiny d not scaled back", "if (tiny) d = d * amax;", "(void)0;"),
+    ("largest error wins", "if (i == 0 || e < best_e) {", "if (i == 0 || e > best_e) {"),
+    ("unweighted fit", "sxl += cube[j] * l[j];\n                    sll += wt[j] * (l[j] * l[j]);",
+     "sxl += v[j] * l[j];\n                    sll += l[j] * l[j];"),
+]
+
+
+def _pins_s():
+    return [(S.test_exact_blocks_are_recovered, ()), (S.test_zero_block_and_sign_of_d, ()),
+            (S.test_brute_force_minimum_and_normal_equation, ()),
+            (S.test_no_worse_than_the_round_rule, ()), (S.test_tiny_blocks_are_scaled_up, ()),
+            (S.test_f16_scales_and_refusals, ()), (S.test_scaling_threshold_is_1e_minus_6, ())]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_S, ids=[m[0] for m in MUTANTS_S])
+def test_planted_search_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    _install(tmp_path, monkeypatch, old, new)
+    failed = []
+    for fn, args in _pins_s():
+        try:
+            fn(*args)
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(fn.__name__)
+    assert failed, f"no pin catches: {name}"
