@@ -16,7 +16,9 @@ launch, SiLU(w1 x) * (w3 x), whose output is w2's input), decode_layer_7 (one
 launch per matrix), gemm_q4_14336x4096,
 gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, writer_q4_14336x4096
 (the weight writer: float32 weights to a Q4_0 f16-scale image by the round
-rule), and copy (a plain device copy, used to calibrate HBM byte counters).
+rule), writer_q4_search_14336x4096 (the same by the least-squares search,
+bound by float32 arithmetic), and copy (a plain device copy, used to
+calibrate HBM byte counters).
 """
 from __future__ import annotations
 
@@ -35,6 +37,14 @@ sys.path.insert(0, ROOT)
 METRIC = "Q4_0/Q8_0 GEMV effective GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+# plain float32 vector operations (multiply, add, round, clamp, each one
+# operation): the published 157.3 TFLOP/s counts a fused multiply-add as two,
+# and an unfused operation takes the same issue slot, so 157.3 / 2 per second
+F32_OPS_PEAK_T = 157.3 / 2
+# float32 operations per 32-weight block of the Q4_0 least-squares search:
+# 13 candidates x (32 x 13 per element + 2 divisions) + 4 x 32 (the largest
+# element, the weights x^2 and x^3)
+SEARCH_OPS_PER_BLOCK = 13 * (32 * 13 + 2) + 4 * 32
 Q8, Q4 = 1, 2
 ROTATE_BYTES = 512 << 20
 
@@ -75,6 +85,9 @@ def workload(name):
     if name == "writer_q4_14336x4096":
         return ("weight writer: float32 14336x4096 -> Q4_0 f16 scales (round rule)", "writer", 4,
                 [(0, Q4, 1, 14336, 4096)], 1)
+    if name == "writer_q4_search_14336x4096":
+        return ("weight writer: float32 14336x4096 -> Q4_0 f16 scales (least-squares search)",
+                "writer", 4, [(0, Q4, 1, 14336, 4096)], 1)
     if name in ("lm_head_b1", "lm_head_b64"):
         b = 1 if name.endswith("b1") else 64
         return (f"shared-classifier LM head Q8_0 248320x1024 f16 scales, f32 hidden, "
@@ -106,6 +119,7 @@ DOMINANT_KERNEL = {
     "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
     "embed_64": ("embed_kernel", "misc.hip"),
     "writer_q4_14336x4096": ("quantize_q4_round_kernel", "writer.hip"),
+    "writer_q4_search_14336x4096": ("quantize_q4_search_kernel", "writer.hip"),
 }
 
 
@@ -212,14 +226,17 @@ def cpu_baseline(kind, config, mats, batch, budget_s):
         b, _ = step_work(kind, mats[:1], batch)
         return {"value": reps * b / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"{reps} gathers of {batch} rows, single thread"}
-    if kind == "writer":
+    if kind in ("writer", "writer_search"):
         w = writer_weights(config, m, r, c)
-        n_rows = 64
+        n_rows = 64 if kind == "writer" else 8
         reps = 0
         t0 = time.perf_counter()
         while True:
             lo = (reps * n_rows) % (r - n_rows)
-            O.quantize_weights(wt, sf, n_rows, c, w[lo:lo + n_rows])
+            if kind == "writer":
+                O.quantize_weights(wt, sf, n_rows, c, w[lo:lo + n_rows])
+            else:
+                O.quantize_q4_search(sf, n_rows, c, w[lo:lo + n_rows])
             reps += 1
             el = time.perf_counter() - t0
             if el >= 0.5 * budget_s or reps >= 10000:
@@ -502,6 +519,8 @@ def run_writer(args, desc, config, mats, stream):
     from block_quant_weight_amd import qmv as Q
     m, wt, sf, r, c = mats[0]
     step_bytes, _ = step_work("writer", mats, 1)
+    search = "search" in args.workload
+    rule = Q.QMV_Q4_SEARCH if search else Q.QMV_Q4_ROUND
     w = torch.from_numpy(writer_weights(config, m, r, c)).cuda()
     ncopies = max(2, -(-ROTATE_BYTES // (4 * r * c)))
     ws = [w] + [w.clone() for _ in range(ncopies - 1)]
@@ -513,7 +532,7 @@ def run_writer(args, desc, config, mats, stream):
     log(f"workload {args.workload}: {desc}; {ncopies} input copies; "
         f"{steps} steps after {warmup} warm-up")
     for i in range(warmup):
-        Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+        Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
     torch.cuda.synchronize()
     if int(status[0].item()) != 0:
         raise RuntimeError("writer reported an unstorable scale")
@@ -522,7 +541,7 @@ def run_writer(args, desc, config, mats, stream):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(steps):
-                Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+                Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
         g.replay()
         torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -532,23 +551,34 @@ def run_writer(args, desc, config, mats, stream):
         g.replay()
     else:
         for i in range(steps):
-            Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status)
+            Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
     kname, ksrc = DOMINANT_KERNEL[args.workload]
-    roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(value / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
-            "launch": {"algorithmic_bytes_per_launch": step_bytes,
-                       "us_per_launch": round(ms_step * 1e3, 3)},
-            "launches_per_step": 1, "algorithmic_bytes_per_step": step_bytes,
-            "flops_per_step": None}
+    launch = {"algorithmic_bytes_per_launch": step_bytes, "us_per_launch": round(ms_step * 1e3, 3)}
+    if search:
+        # bound by float32 arithmetic, not by memory
+        ops = SEARCH_OPS_PER_BLOCK * r * c // 32
+        achieved = ops / (ms_step * 1e-3) / 1e12
+        launch["f32_ops_per_launch"] = ops
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(F32_OPS_PEAK_T, 3),
+                "unit": "Tops/s (float32, unfused)", "frac": round(achieved / F32_OPS_PEAK_T, 4),
+                "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
+                "launch": launch, "launches_per_step": 1,
+                "algorithmic_bytes_per_step": step_bytes, "flops_per_step": ops}
+    else:
+        roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
+                "launch": launch, "launches_per_step": 1,
+                "algorithmic_bytes_per_step": step_bytes, "flops_per_step": None}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores")
-        cpu = cpu_baseline("writer", config, mats, 1, args.cpu_budget)
+        cpu = cpu_baseline("writer_search" if search else "writer", config, mats, 1,
+                           args.cpu_budget)
     wl = {"workload": args.workload, "description": desc, "batch": 1,
           "matrices": [{"wtype": "Q8_0" if wt == Q8 else "Q4_0", "scales": "f16" if sf else "f32",
                         "rows": r, "cols": c}],

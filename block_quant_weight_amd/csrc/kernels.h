@@ -58,10 +58,11 @@ hipError_t launch_gguf_repack(uint32_t wtype, const void* src, uint64_t nblocks,
 
 // Writer rules over nblocks blocks of float32 weights w: quants to q, then
 // q_pad (< 64) zero bytes, scales to d (float or f16 bits); *bad cleared,
-// then set to 1 when an f16 scale does not fit.  Kernels only (no memset).
-hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, const float* w,
-                                   uint64_t nblocks, uint8_t* q, uint32_t q_pad, void* d,
-                                   uint32_t* bad, hipStream_t stream);
+// then set to 1 when a scale cannot be stored.  rule 0: Q8_0 or the Q4_0
+// round rule; 1: the Q4_0 least-squares search.  Kernels only (no memset).
+hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule,
+                                   const float* w, uint64_t nblocks, uint8_t* q, uint32_t q_pad,
+                                   void* d, uint32_t* bad, hipStream_t stream);
 
 // Activation Q8_0 quantizer over n floats (n % 32 == 0).
 hipError_t launch_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,

@@ -262,18 +262,19 @@ int qmv_embed_rows(qmv_handle h, const int32_t* ids, uint32_t n, float* out,
                                            static_cast<hipStream_t>(stream)));
 }
 
-int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
-                         const float* w, void* image, uint64_t image_bytes, uint32_t* status,
-                         void* stream) {
+int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule, uint32_t rows,
+                         uint32_t cols, const float* w, void* image, uint64_t image_bytes,
+                         uint32_t* status, void* stream) {
     qmv::Layout L;
     int st = qmv::compute_layout(wtype, scale_f16, rows, cols, &L);
     if (st != QMV_OK) return st;
+    if (rule > 1 || (rule == 1 && wtype != QMV_Q4_0)) return QMV_E_ARG;
     if (w == nullptr || image == nullptr || status == nullptr) return QMV_E_ARG;
     if (!aligned16(w) || !aligned16(image) || image_bytes < L.min_span) return QMV_E_ARG;
     if ((reinterpret_cast<uintptr_t>(status) & 3u) != 0) return QMV_E_ARG;
     uint8_t* img = static_cast<uint8_t*>(image);
     return device_status(qmv::launch_quantize_weights(
-        wtype, scale_f16, w, uint64_t{rows} * (cols / 32), img,
+        wtype, scale_f16, rule, w, uint64_t{rows} * (cols / 32), img,
         static_cast<uint32_t>(L.d_offset - L.q_bytes), img + L.d_offset, status,
         static_cast<hipStream_t>(stream)));
 }

@@ -21,6 +21,13 @@
 //     nibble = min(15, trunc(x * (1 / d) + 8.5)), 1 / d taken as 0 when
 //     d = 0 or when 1 / d overflows (|d| < 2^-128); with f16 scales d is
 //     stored as fl16(d), the nibbles use the float32 d.
+//   - Q4_0 least-squares search: the largest element mx mapped to each
+//     candidate level L = -6.0, -6.2, ..., -8.4; levels rint(x * (L / mx))
+//     clamped to [-8, 7]; d = sum w x l / sum w l^2 with w = x^2; the
+//     candidate of smallest weighted error sum w (x - d l)^2 wins (the first
+//     on ties); a block below 1e-6 is divided by its largest magnitude
+//     first and d multiplied back; the sums run in element order; a fit
+//     that is not finite, or with f16 scales above 65504, is refused.
 // An f16 Q8_0 scale that rounds to 0 gives q = 0 (the weights are 0 either
 // way).
 #include "device_common.h"
@@ -164,6 +171,109 @@ __global__ __launch_bounds__(256) void quantize_q4_round_kernel(const float* __r
     }
 }
 
+// The 13 candidate levels of the least-squares search (the float32 nearest
+// each decimal value).
+__constant__ float kSearchLevel[13] = {-6.0f, -6.2f, -6.4f, -6.6f, -6.8f, -7.0f, -7.2f,
+                                       -7.4f, -7.6f, -7.8f, -8.0f, -8.2f, -8.4f};
+
+__device__ __forceinline__ float search_level(float v, float iscale) {
+    return fminf(fmaxf(rintf(v * iscale), -8.f), 7.f);
+}
+
+// Q4_0 least-squares search, one thread per block: 13 candidates of 32
+// levels, each scored by its weighted error (about 400 float32 operations
+// per candidate); the winner's levels are computed again for the store.
+template <bool SF16>
+__global__ __launch_bounds__(256) void quantize_q4_search_kernel(const float* __restrict__ w,
+                                                                 uint64_t nblocks, uint8_t* __restrict__ q,
+                                                                 void* __restrict__ d_out,
+                                                                 uint32_t* __restrict__ bad) {
+    const uint64_t k = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (k >= nblocks) return;
+    float v[32];
+    const float4* xp = reinterpret_cast<const float4*>(w + 32 * k);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 t = xp[i];
+        v[4 * i] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+    }
+    float amax = 0.f, mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float a = fabsf(v[j]);
+        if (a > amax) {
+            amax = a;
+            mx = v[j];
+        }
+    }
+    float d = 0.f, iscale = 0.f;  // iscale 0: every level 0 (nibble 8)
+    if (amax != 0.f) {
+        const bool tiny = amax < 1e-6f;
+        if (tiny) {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) v[j] = v[j] / amax;
+            mx = mx / amax;
+        }
+        float wt[32], cube[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            wt[j] = v[j] * v[j];
+            cube[j] = wt[j] * v[j];
+        }
+        float best_e = 0.f;
+#pragma unroll 1
+        for (int i = 0; i < 13; ++i) {
+            const float is = kSearchLevel[i] / mx;
+            float l[32];
+            float sxl = 0.f, sll = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                l[j] = search_level(v[j], is);
+                sxl = sxl + cube[j] * l[j];
+                sll = sll + wt[j] * (l[j] * l[j]);
+            }
+            const float dc = sxl / sll;
+            float e = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const float r = v[j] - dc * l[j];
+                e = e + wt[j] * (r * r);
+            }
+            if (i == 0 || e < best_e) {
+                best_e = e;
+                d = dc;
+                iscale = is;
+            }
+        }
+        if (tiny) d = d * amax;
+        if (!__builtin_isfinite(d)) *bad = 1u;
+    }
+    uint32_t packed[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = 4 * i + c;
+            const uint32_t n0 = static_cast<uint32_t>(search_level(v[j], iscale) + 8.f);
+            const uint32_t n1 = static_cast<uint32_t>(search_level(v[j + 16], iscale) + 8.f);
+            word |= (n0 | (n1 << 4)) << (8 * c);
+        }
+        packed[i] = word;
+    }
+    *reinterpret_cast<uint4*>(q + 16 * k) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if constexpr (SF16) {
+        const uint16_t db = f16_bits(d);
+        if ((db & 0x7FFFu) >= 0x7C00u) *bad = 1u;
+        static_cast<uint16_t*>(d_out)[k] = db;
+    } else {
+        static_cast<float*>(d_out)[k] = d;
+    }
+}
+
 // Clears the status word and the zero padding between the q and d arrays
 // (a kernel rather than memsets, so the call can be captured in a graph).
 __global__ void writer_prepare_kernel(uint32_t* __restrict__ bad, uint8_t* __restrict__ pad,
@@ -189,10 +299,10 @@ hipError_t launch_gguf_repack(uint32_t wtype, const void* src, uint64_t nblocks,
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, const float* w,
-                                   uint64_t nblocks, uint8_t* q, uint32_t q_pad, void* d,
-                                   uint32_t* bad, hipStream_t s) {
-    if (q_pad >= 64) return hipErrorInvalidValue;
+hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule,
+                                   const float* w, uint64_t nblocks, uint8_t* q, uint32_t q_pad,
+                                   void* d, uint32_t* bad, hipStream_t s) {
+    if (q_pad >= 64 || (rule != 0 && wtype != kQ4)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(writer_prepare_kernel, dim3(1), dim3(64), 0, s, bad,
                        q + nblocks * (wtype == kQ4 ? 16 : 32), q_pad);
     if (wtype == kQ8 && !scale_f16)
@@ -200,7 +310,12 @@ hipError_t launch_quantize_weights(uint32_t wtype, uint32_t scale_f16, const flo
     const uint64_t grid = (nblocks + 255) / 256;
     if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const dim3 g(static_cast<uint32_t>(grid)), b(256);
-    if (wtype == kQ8)
+    if (rule != 0) {
+        if (scale_f16)
+            hipLaunchKernelGGL(quantize_q4_search_kernel<true>, g, b, 0, s, w, nblocks, q, d, bad);
+        else
+            hipLaunchKernelGGL(quantize_q4_search_kernel<false>, g, b, 0, s, w, nblocks, q, d, bad);
+    } else if (wtype == kQ8)
         hipLaunchKernelGGL(quantize_q8_f16_kernel, g, b, 0, s, w, nblocks, reinterpret_cast<int8_t*>(q),
                            static_cast<uint16_t*>(d), bad);
     else if (scale_f16)

@@ -58,7 +58,7 @@ def lib():
             "qmv_status_str": ([i32], ctypes.c_char_p),
             "qmv_gguf_span": ([u32, u32, u32, pu64], i32),
             "qmv_upload_gguf": ([vp, vp, u64, vp], i32),
-            "qmv_quantize_weights": ([u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
+            "qmv_quantize_weights": ([u32, u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
             "qmv_gemv_gated": ([vp, vp, u32, vp, vp, u32, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -167,12 +167,18 @@ def qmv_upload_gguf(h: QmvHandle, src, nbytes=None, stream=None):
     _check(st, "qmv_upload_gguf")
 
 
-def qmv_quantize_weights(wtype, scale_f16, w, image, status=None, stream=None):
+QMV_Q4_ROUND = 0
+QMV_Q4_SEARCH = 1
+
+
+def qmv_quantize_weights(wtype, scale_f16, w, image, status=None, stream=None,
+                         rule=QMV_Q4_ROUND):
     """w: float32 [rows, cols] on the GPU; image: uint8 GPU tensor of at least
-    min_span bytes, receiving the .mlb bytes.  With status (an int32/uint32
-    GPU tensor of >= 1 element) the call only enqueues work and status[0]
-    tells, once done, whether a scale did not fit f16 (1); without it the
-    call waits and raises QmvError(QMV_E_FORMAT) in that case."""
+    min_span bytes, receiving the .mlb bytes; rule QMV_Q4_SEARCH selects the
+    Q4_0 least-squares writer.  With status (an int32/uint32 GPU tensor of
+    >= 1 element) the call only enqueues work and status[0] tells, once done,
+    whether a scale could not be stored (1); without it the call waits and
+    raises QmvError(QMV_E_FORMAT) in that case."""
     import torch
     rows, cols = w.shape
     pw = _dev(w, torch.float32, rows * cols, "w")
@@ -183,13 +189,13 @@ def qmv_quantize_weights(wtype, scale_f16, w, image, status=None, stream=None):
     if own:
         status = torch.empty(1, dtype=torch.int32, device=image.device)
     ps = _dev(status, status.dtype, 1, "status")
-    st = lib().qmv_quantize_weights(wtype, scale_f16, rows, cols, pw, pi, image.numel(), ps,
-                                    _stream(stream))
+    st = lib().qmv_quantize_weights(wtype, scale_f16, rule, rows, cols, pw, pi, image.numel(),
+                                    ps, _stream(stream))
     _check(st, "qmv_quantize_weights")
     if own:
         torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
         if int(status[0].item()) != 0:
-            raise QmvError(QMV_E_FORMAT, "qmv_quantize_weights: a scale does not fit f16")
+            raise QmvError(QMV_E_FORMAT, "qmv_quantize_weights: a scale cannot be stored")
 
 
 def qmv_destroy(h: QmvHandle):

@@ -264,25 +264,37 @@ int qmv_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d,
  *   - Q8_0, f16 scales: d = amax / 127 rounded to the nearest f16, then
  *     q = trunc(x * (1 / d) + copysign(0.5, x)) against that rounded d,
  *     clamped to [-127, 127] (q = 0 when d rounds to 0);
- *   - Q4_0, the page's "round" rule: d = (the first element of largest
- *     magnitude) / -8, nibble = min(15, trunc(x * (1 / d) + 8.5)) with
- *     1 / d taken as 0 when d = 0 or when it overflows (|d| < 2^-128);
- *     with f16 scales d is stored rounded to
- *     f16 while the nibbles use the float32 d.  (The page's least-squares
- *     Q4_0 search is not provided.)
+ *   - Q4_0, rule QMV_Q4_ROUND, the page's "round" rule: d = (the first
+ *     element of largest magnitude) / -8, nibble = min(15, trunc(x * (1 /
+ *     d) + 8.5)) with 1 / d taken as 0 when d = 0 or when it overflows
+ *     (|d| < 2^-128); with f16 scales d is stored rounded to f16 while the
+ *     nibbles use the float32 d;
+ *   - Q4_0, rule QMV_Q4_SEARCH, the page's least-squares writer: the first
+ *     element of largest magnitude mx is mapped to each of the 13 levels
+ *     L = -6.0, -6.2, ..., -8.4; levels rint(x * (L / mx)) (half to even)
+ *     clamped to [-8, 7]; d = sum w x l / sum w l^2 with w = x^2, summed in
+ *     element order; the candidate of smallest sum w (x - d l)^2 wins, the
+ *     first on ties; a block whose largest magnitude is below 1e-6 is
+ *     divided by it first and d multiplied back; nibble = level + 8; with
+ *     f16 scales the fitted d is rounded to f16.
+ * rule: QMV_Q4_ROUND (0) for every storage type, QMV_Q4_SEARCH (1) for
+ * Q4_0 only.
  * image (device, 16-byte aligned, at least min_span bytes) receives the
  * bytes; they can be written to a file or uploaded with qmv_upload.
  * status (a device uint32, 4-byte aligned) is set to 0, and to 1 if some
- * f16 scale is above 65504 and cannot be stored (the image is then not a
- * valid file's); read it once the work on `stream` is done.  Like the
- * compute calls it only enqueues kernels (no allocation, no memset), so it
- * can be captured in a graph.
+ * scale cannot be stored: an f16 scale above 65504, or a least-squares fit
+ * that is not finite (weights above about 2^42, whose float32 cubes
+ * overflow); the image is then not a valid file's.  Read it once the work
+ * on `stream` is done.  Like the compute calls it only enqueues kernels (no
+ * allocation, no memset), so it can be captured in a graph.
  * Errors: QMV_E_FORMAT (wtype, scale_f16), QMV_E_SHAPE, QMV_E_ARG (null or
- * misaligned pointer, image too small), QMV_E_DEVICE.
+ * misaligned pointer, image too small, rule > 1 or QMV_Q4_SEARCH with
+ * Q8_0), QMV_E_DEVICE.
  */
-int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
-                         const float *w, void *image, uint64_t image_bytes, uint32_t *status,
-                         void *stream);
+enum { QMV_Q4_ROUND = 0, QMV_Q4_SEARCH = 1 };
+int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule, uint32_t rows,
+                         uint32_t cols, const float *w, void *image, uint64_t image_bytes,
+                         uint32_t *status, void *stream);
 
 /*
  * Per-block integer dot products of the weight quants with quantized

@@ -192,14 +192,17 @@ def test_gguf_upload_host_checks():
 def test_quantize_weights_host_checks():
     L = Q.lib()
     p = ctypes.c_void_p(4096)
-    assert L.qmv_quantize_weights(3, 0, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
-    assert L.qmv_quantize_weights(1, 2, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
-    assert L.qmv_quantize_weights(1, 0, 1, 48, p, p, 1 << 20, p, None) == Q.QMV_E_SHAPE
-    assert L.qmv_quantize_weights(1, 0, 1, 32, None, p, 1 << 20, p, None) == Q.QMV_E_ARG
-    assert L.qmv_quantize_weights(1, 0, 1, 32, p, p, 1 << 20, None, None) == Q.QMV_E_ARG
-    assert L.qmv_quantize_weights(1, 0, 1, 32, ctypes.c_void_p(4100), p, 1 << 20, p,
+    assert L.qmv_quantize_weights(3, 0, 0, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
+    assert L.qmv_quantize_weights(1, 2, 0, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_FORMAT
+    assert L.qmv_quantize_weights(1, 0, 0, 1, 48, p, p, 1 << 20, p, None) == Q.QMV_E_SHAPE
+    assert L.qmv_quantize_weights(1, 0, 0, 1, 32, None, p, 1 << 20, p, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 0, 0, 1, 32, p, p, 1 << 20, None, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 0, 0, 1, 32, ctypes.c_void_p(4100), p, 1 << 20, p,
                                   None) == Q.QMV_E_ARG
-    assert L.qmv_quantize_weights(1, 0, 1, 32, p, p, 1 << 20, ctypes.c_void_p(4098),
+    assert L.qmv_quantize_weights(1, 0, 0, 1, 32, p, p, 1 << 20, ctypes.c_void_p(4098),
                                   None) == Q.QMV_E_ARG
     need = Q.qmv_span(1, 1, 1, 32)["min_span"]
-    assert L.qmv_quantize_weights(1, 1, 1, 32, p, p, need - 1, p, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(1, 1, 0, 1, 32, p, p, need - 1, p, None) == Q.QMV_E_ARG
+    # the least-squares search is a Q4_0 rule; rules above 1 do not exist
+    assert L.qmv_quantize_weights(1, 0, 1, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_ARG
+    assert L.qmv_quantize_weights(2, 0, 2, 1, 32, p, p, 1 << 20, p, None) == Q.QMV_E_ARG

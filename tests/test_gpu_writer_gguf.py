@@ -133,3 +133,62 @@ def test_writer_image_uploads_and_multiplies():
             assert ok, worst
         finally:
             Q.qmv_destroy(h)
+
+
+# ---- the Q4_0 least-squares writer ------------------------------------------
+
+def search_rows_ref(w, sf, rows_sel):
+    """Oracle image bytes (q rows, d entries) of the selected rows: rows are
+    quantized independently, so a sample of rows checks the whole image."""
+    C = w.shape[1]
+    st, ref = O.quantize_q4_search(sf, len(rows_sel), C, w[rows_sel])
+    assert st == "ok"
+    sp = Q.qmv_span(2, sf, len(rows_sel), C)
+    q = ref[:sp["q_bytes"]].reshape(len(rows_sel), C // 2)
+    d = ref[sp["d_offset"]:sp["d_offset"] + sp["d_bytes"]].reshape(len(rows_sel), -1)
+    return q, d
+
+
+@pytest.mark.parametrize("sf", [0, 1])
+@pytest.mark.parametrize("R,C", [(5, 64), (300, 1024), (14336, 4096)])
+def test_search_writer_bit_exact(sf, R, C):
+    import torch
+    w = writer_weights(2000 + R + sf, R, C)
+    sp = Q.qmv_span(2, sf, R, C)
+    n = sp["min_span"]
+    img = torch.full((n + 64,), 0xAB, dtype=torch.uint8, device="cuda")
+    Q.qmv_quantize_weights(2, sf, torch.from_numpy(w).cuda(), img, rule=Q.QMV_Q4_SEARCH)
+    got = img.cpu().numpy()
+    assert np.all(got[n:] == 0xAB)                # nothing written past min_span
+    if R * C <= 300 * 1024:
+        st, ref = O.quantize_q4_search(sf, R, C, w)
+        assert st == "ok"
+        assert np.array_equal(got[:n], ref[:n])
+        return
+    sel = K.sample_rows(R, 400, seed=R)
+    q_ref, d_ref = search_rows_ref(w, sf, sel)
+    q_got = got[:sp["q_bytes"]].reshape(R, C // 2)[sel]
+    d_got = got[sp["d_offset"]:sp["d_offset"] + sp["d_bytes"]].reshape(R, -1)[sel]
+    assert np.array_equal(q_got, q_ref)
+    assert np.array_equal(d_got, d_ref)
+    assert not got[sp["q_bytes"]:sp["d_offset"]].any()   # the zero pad
+
+
+def test_search_writer_refusals():
+    import torch
+    R, C = 4, 64
+    w = np.random.default_rng(9).standard_normal((R, C)).astype(np.float32)
+    big = w.copy()
+    big[2, 7] = 9e5                               # fitted |d| ~ 1.1e5: not an f16
+    huge = w.copy()
+    huge[1, 50] = 1e13                            # float32 cubes overflow
+    for x, sf in ((big, 1), (huge, 0), (huge, 1)):
+        assert O.quantize_q4_search(sf, R, C, x)[0] == "format"
+        img = torch.zeros(Q.qmv_span(2, sf, R, C)["min_span"], dtype=torch.uint8, device="cuda")
+        with pytest.raises(Q.QmvError) as e:
+            Q.qmv_quantize_weights(2, sf, torch.from_numpy(x).cuda(), img, rule=Q.QMV_Q4_SEARCH)
+        assert e.value.status == Q.QMV_E_FORMAT
+    st, ref = O.quantize_q4_search(0, R, C, big)
+    img = torch.zeros(Q.qmv_span(2, 0, R, C)["min_span"], dtype=torch.uint8, device="cuda")
+    Q.qmv_quantize_weights(2, 0, torch.from_numpy(big).cuda(), img, rule=Q.QMV_Q4_SEARCH)
+    assert np.array_equal(img.cpu().numpy(), ref[:img.numel()])
