@@ -64,6 +64,8 @@ def lib():
         L.orc_quantize_q8.restype = None
         L.orc_block_dots.argtypes = [vp, u32, u64, u64, vp, vp]
         L.orc_block_dots.restype = None
+        L.orc_gemm_q8act.argtypes = [vp, u32, u32, u64, u64, vp, vp, u64, vp, u64, vp, vp]
+        L.orc_gemm_q8act.restype = None
         L.orc_class_wtype.argtypes = [u32, u32, u32, u32, ctypes.POINTER(u32)]
         L.orc_class_wtype.restype = i32
         L.orc_check_image.argtypes = [u32, u32, u64, u64, vp, u64]
@@ -195,6 +197,52 @@ def block_dots(img, wtype, rows, cols, xq: np.ndarray) -> np.ndarray:
     s = np.zeros((rows, cols // 32), dtype=np.int32)
     lib().orc_block_dots(_ptr(img), wtype, rows, cols, _ptr(xq), _ptr(s))
     return s
+
+
+def gemm_q8act(img, wtype, scale_f16, rows, cols, xq, dx, sel=None, threads: int = 1):
+    """(ref, bound), float64 [batch][len(sel)]: the product on Q8_0-quantized
+    activations (xq int8 [batch][cols], dx float32 [batch][cols/32])."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    dx = np.ascontiguousarray(dx, dtype=np.float32)
+    if xq.ndim == 1:
+        xq = xq.reshape(1, -1)
+    batch = xq.shape[0]
+    assert xq.shape[1] == cols and dx.size == batch * (cols // 32)
+    if sel is None:
+        sel = np.arange(rows, dtype=np.int64)
+    sel = np.ascontiguousarray(sel, dtype=np.int64)
+    L = lib()
+
+    def run(part):
+        p = np.ascontiguousarray(part)
+        ref = np.zeros((batch, p.size), dtype=np.float64)
+        bnd = np.zeros((batch, p.size), dtype=np.float64)
+        L.orc_gemm_q8act(_ptr(img), wtype, scale_f16, rows, cols, _ptr(xq), _ptr(dx), batch,
+                         _ptr(p), p.size, _ptr(ref), _ptr(bnd))
+        return ref, bnd
+
+    if threads <= 1 or sel.size < 2 * threads:
+        return run(sel)
+    parts = np.array_split(sel, threads)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        res = list(ex.map(run, parts))
+    return (np.concatenate([r for r, _ in res], axis=1),
+            np.concatenate([b for _, b in res], axis=1))
+
+
+def q8act_within_tolerance(y, ref, bound, cols):
+    """Parity predicate of the product on quantized activations: the block
+    sums are exact integers, so the only error is float32 rounding of the
+    combine, each block's fl(dw dx) and its multiply-add into the running
+    sum: |y - ref| <= (nb + 2) 2^-23 bound, nb = cols / 32 blocks (twice
+    the first-order bound).  Returns (ok, worst ratio err / tolerance)."""
+    y = np.asarray(y, dtype=np.float64)
+    tol = (cols // 32 + 2) * 2.0 ** -23 * bound
+    err = np.abs(y - ref)
+    ok = bool((err <= tol).all())
+    pos = tol > 0
+    worst = float((err[pos] / tol[pos]).max()) if pos.any() else 0.0
+    return ok, worst
 
 
 def class_wtype(file_wtype, q8_mask, class_bit, shared_classifier):

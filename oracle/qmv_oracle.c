@@ -309,6 +309,44 @@ void orc_block_dots(const uint8_t *img, uint32_t wtype, uint64_t rows,
 }
 
 /*
+ * Product on Q8_0-quantized activations (the page's CPU path: activations
+ * quantized per block of 32 by the "Quantization rule", then per-block
+ * integer dot products): for each selected row r and token t,
+ *   ref[t][r]   = sum_b dw[r,b] * dx[t,b] * s[t,r,b],
+ *   bound[t][r] = sum_b |dw[r,b] * dx[t,b] * s[t,r,b]|,
+ *   s[t,r,b]    = sum_j v[r,32b+j] * xq[t,32b+j]   (exact, int32),
+ * in binary64 in block order, dw the decoded scale and dx[t,b] the
+ * activation block's scale.  xq is int8 [batch][cols], dx float32
+ * [batch][cols/32]; ref and bound are [batch][n_sel].
+ */
+void orc_gemm_q8act(const uint8_t *img, uint32_t wtype, uint32_t scale_f16,
+                    uint64_t rows, uint64_t cols, const int8_t *xq, const float *dx,
+                    uint64_t batch, const int64_t *sel, uint64_t n_sel, double *ref,
+                    double *bound) {
+    uint64_t span[5];
+    if (orc_span(wtype, scale_f16, rows, cols, span) != ORC_OK) return;
+    uint64_t nb = cols / 32;
+    for (uint64_t t = 0; t < batch; ++t) {
+        for (uint64_t i = 0; i < n_sel; ++i) {
+            uint64_t r = (uint64_t)sel[i];
+            double acc = 0.0, bnd = 0.0;
+            for (uint64_t b = 0; b < nb; ++b) {
+                int32_t sb = 0;
+                for (uint64_t j = 0; j < 32; ++j)
+                    sb += orc_quant(img, wtype, cols, r, 32 * b + j) *
+                          (int32_t)xq[t * cols + 32 * b + j];
+                double dw = (double)orc_scale(img, span[1], scale_f16, r * nb + b);
+                double term = dw * (double)dx[t * nb + b] * (double)sb;
+                acc += term;
+                bnd += fabs(term);
+            }
+            ref[t * n_sel + i] = acc;
+            bound[t * n_sel + i] = bnd;
+        }
+    }
+}
+
+/*
  * Storage type of one matrix class (the q8_mask paragraph).  Class bits:
  * 1 tok_emb, 2 wcls, 4 wq/wk (wg, lqkv), 8 wv (lz), 16 wo (lout),
  * 32 w1/w3, 64 w2.  A Q8_0 file stores every matrix as Q8_0.  In a Q4_0

@@ -216,3 +216,40 @@ def test_planted_search_mistake_is_caught(tmp_path, monkeypatch, name, old, new)
         except Exception:  # noqa: BLE001 - any failure of a pin counts
             failed.append(fn.__name__)
     assert failed, f"no pin catches: {name}"
+
+
+# ---- the product on Q8_0-quantized activations -------------------------------
+
+import test_oracle_q8act as A8  # noqa: E402
+
+MUTANTS_A = [
+    ("activation scale of token 0", "(double)dx[t * nb + b]", "(double)dx[b]"),
+    ("next block's weight scale", "orc_scale(img, span[1], scale_f16, r * nb + b)",
+     "orc_scale(img, span[1], scale_f16, r * nb + (b + 1) % nb)"),
+    ("bound without absolute values", "bnd += fabs(term);", "bnd += term;"),
+    ("activation quants unsigned", "(int32_t)xq[t * cols + 32 * b + j]",
+     "(int32_t)(uint8_t)xq[t * cols + 32 * b + j]"),
+    ("block of 31", "for (uint64_t j = 0; j < 32; ++j)\n                    sb +=",
+     "for (uint64_t j = 0; j < 31; ++j)\n                    sb +="),
+]
+
+
+def _pins_a():
+    out = [(A8.test_quantized_activations_stay_within_the_quantizer_bound, ())]
+    for wt in (2, 1):
+        out.append((A8.test_exact_rationals, (wt,)))
+    for wt, sf in ((2, 1), (1, 0)):
+        out.append((A8.test_power_of_two_scales_equal_the_plain_product, (wt, sf)))
+    return out
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS_A, ids=[m[0] for m in MUTANTS_A])
+def test_planted_q8act_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    _install(tmp_path, monkeypatch, old, new)
+    failed = []
+    for fn, args in _pins_a():
+        try:
+            fn(*args)
+        except Exception:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(fn.__name__)
+    assert failed, f"no pin catches: {name}"
