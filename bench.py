@@ -17,8 +17,10 @@ launch per matrix), gemm_q4_14336x4096,
 gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, writer_q4_14336x4096
 (the weight writer: float32 weights to a Q4_0 f16-scale image by the round
 rule), writer_q4_search_14336x4096 (the same by the least-squares search,
-bound by float32 arithmetic), and copy (a plain device copy, used to
-calibrate HBM byte counters).
+bound by float32 arithmetic), gemm_q8act_q4_14336x4096 and
+gemm_q8act_q8_4096x14336 (the prefill shapes on the int8 path: float32
+activations quantized to Q8_0, then the int8 matrix-core product), and copy
+(a plain device copy, used to calibrate HBM byte counters).
 """
 from __future__ import annotations
 
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Q4_0/Q8_0 GEMV effective GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
 # plain float32 vector operations (multiply, add, round, clamp, each one
 # operation): the published 157.3 TFLOP/s counts a fused multiply-add as two,
 # and an unfused operation takes the same issue slot, so 157.3 / 2 per second
@@ -82,6 +85,14 @@ def workload(name):
     if name == "gemm_q8_4096x14336":
         return ("prefill GEMM Q8_0 4096x14336 f32 scales x bf16 [512x14336]", "gemm", 4,
                 [(1, Q8, 0, 4096, 14336)], 512)
+    if name == "gemm_q8act_q4_14336x4096":
+        return ("prefill on quantized activations: float32 [512x4096] -> Q8_0, then Q4_0 "
+                "14336x4096 f16 scales on the int8 matrix cores", "gemm_q8", 4,
+                [(0, Q4, 1, 14336, 4096)], 512)
+    if name == "gemm_q8act_q8_4096x14336":
+        return ("prefill on quantized activations: float32 [512x14336] -> Q8_0, then Q8_0 "
+                "4096x14336 f32 scales on the int8 matrix cores", "gemm_q8", 4,
+                [(1, Q8, 0, 4096, 14336)], 512)
     if name == "writer_q4_14336x4096":
         return ("weight writer: float32 14336x4096 -> Q4_0 f16 scales (round rule)", "writer", 4,
                 [(0, Q4, 1, 14336, 4096)], 1)
@@ -117,6 +128,8 @@ DOMINANT_KERNEL = {
     "lm_head_b64": ("gemv_mfma_kernel (f16 operands)", "gemv_mfma.hip"),
     "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm.hip"),
     "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
+    "gemm_q8act_q4_14336x4096": ("gemm_q8act_kernel", "gemm_i8.hip"),
+    "gemm_q8act_q8_4096x14336": ("gemm_q8act_kernel", "gemm_i8.hip"),
     "embed_64": ("embed_kernel", "misc.hip"),
     "writer_q4_14336x4096": ("quantize_q4_round_kernel", "writer.hip"),
     "writer_q4_search_14336x4096": ("quantize_q4_search_kernel", "writer.hip"),
@@ -156,6 +169,9 @@ def step_work(kind, mats, batch, groups=None, gated=False):
             flops += 2 * r * c * batch
         elif kind == "gemm":
             byts += w + 2 * c * batch + 4 * r * batch
+            flops += 2 * r * c * batch
+        elif kind == "gemm_q8":
+            byts += w + 4 * c * batch + 4 * r * batch
             flops += 2 * r * c * batch
         elif kind == "writer":
             byts += 4 * r * c + w          # float32 weights in, the image out
@@ -244,6 +260,25 @@ def cpu_baseline(kind, config, mats, batch, budget_s):
         byts = reps * n_rows * c * 4 + reps * n_rows * matrix_bytes(wt, sf, 1, c)
         return {"value": byts / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"{reps} x {n_rows} rows of {r} (single thread, {el:.1f} s)"}
+    if kind == "gemm_q8":
+        x = synth.act_f32(synth.rng(config, m, synth.STREAM_ACT), batch, c)
+        xq = np.zeros((batch, c), dtype=np.int8)
+        dx = np.zeros((batch, c // 32), dtype=np.float32)
+        for t in range(batch):
+            xq[t], dx[t] = O.quantize_q8(x[t])
+        probe = np.arange(min(r, 4), dtype=np.int64)
+        t0 = time.perf_counter()
+        O.gemm_q8act(img, wt, sf, r, c, xq, dx, sel=probe, threads=1)
+        per_row = max((time.perf_counter() - t0) / probe.size, 1e-7)
+        n_rows = int(min(r, max(threads, 0.5 * budget_s * threads / per_row)))
+        sel = np.linspace(0, r - 1, n_rows).astype(np.int64)
+        t0 = time.perf_counter()
+        O.gemm_q8act(img, wt, sf, r, c, xq, dx, sel=sel, threads=threads)
+        el = time.perf_counter() - t0
+        ops = 2 * n_rows * c * batch
+        return {"value": ops / el / 1e12, "unit": "TOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"{n_rows} of {r} rows x {batch} tokens (int32 block sums, f64 "
+                          f"combine, {threads} threads, {el:.1f} s)"}
     if kind == "gemm":
         x = synth.act_bf16(synth.rng(config, m, synth.STREAM_ACT), batch, c)
     else:
@@ -332,7 +367,7 @@ def main():
     ncopies = max(2, -(-ROTATE_BYTES // set_bytes))
     if kind == "embed":
         ncopies = 1   # a gather touches 64 rows; rows are drawn afresh per step
-    steps = args.steps if args.steps is not None else (200 if kind == "gemm" else 1000)
+    steps = args.steps if args.steps is not None else (200 if kind in ("gemm", "gemm_q8") else 1000)
     warmup = args.warmup if args.warmup is not None else 20
     log(f"workload {args.workload}: {desc}; {ncopies} weight copies; "
         f"{steps} steps after {warmup} warm-up")
@@ -359,9 +394,14 @@ def main():
         if kind == "gemm":
             xb = synth.act_bf16(g, batch, c)
             xs.append(torch.from_numpy(xb.view(np.int16)).cuda().view(torch.bfloat16))
-        elif kind == "gemv":
+        elif kind in ("gemv", "gemm_q8"):
             xs.append(torch.from_numpy(synth.act_f32(g, batch, c)).cuda())
         ys.append(torch.empty((batch, r), dtype=torch.float32, device="cuda"))
+    # the int8 path's quantized activations (written by each step)
+    xqs = [torch.empty((batch, c), dtype=torch.int8, device="cuda") for (_, _, _, _, c) in mats] \
+        if kind == "gemm_q8" else []
+    dxs = [torch.empty((batch, c // 32), dtype=torch.float32, device="cuda")
+           for (_, _, _, _, c) in mats] if kind == "gemm_q8" else []
     id_sets = []
     if kind == "embed":
         r = mats[0][3]
@@ -391,6 +431,9 @@ def main():
                 Q.qmv_gemv(h, xs[j], ys[j])
             elif kind == "gemm":
                 Q.qmv_gemm(h, xs[j], ys[j])
+            elif kind == "gemm_q8":
+                Q.qmv_quantize_q8(xs[j], xqs[j], dxs[j])
+                Q.qmv_gemm_q8(h, xqs[j], dxs[j], ys[j])
             else:
                 Q.qmv_embed_rows(h, id_sets[i % len(id_sets)], out)
 
@@ -425,6 +468,11 @@ def main():
         value, unit = step_flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
         bound, peak, runit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
         dtype = "bf16"
+    elif kind == "gemm_q8":
+        value, unit = step_flops / (ms_step * 1e-3) / 1e12, "TOP/s"
+        bound, peak, runit = "mfma", INT8_PEAK_TOPS, "TOP/s (int8)"
+        dtype = "i8"
+        launches_per_step = 2 * len(mats)
     else:
         value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
         bound, peak, runit = "hbm", HBM_PEAK_GBS, "GB/s"
@@ -479,6 +527,34 @@ def main():
         dom_desc = {"matrices": [LAYER[j][0] for j in gr] if args.workload.startswith("decode")
                     else gr, "algorithmic_bytes_per_launch": dom_bytes,
                     "us_per_launch": round(dom_ms * 1e3, 3), "copies_rotated": dom_copies}
+    elif kind == "gemm_q8":
+        # the int8 product alone (its activations quantized once, before the
+        # graph), the same rotation and timing
+        h0 = handles[0][0]
+        for j in range(len(mats)):
+            Q.qmv_quantize_q8(xs[j], xqs[j], dxs[j])
+
+        def launch(i):
+            Q.qmv_gemm_q8(handles[i % ncopies][0], xqs[0], dxs[0], ys[0])
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=stream):
+            for i in range(steps):
+                launch(warmup + i)
+        g2.replay()
+        torch.cuda.synchronize()
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        g2.replay()
+        e3.record(stream)
+        torch.cuda.synchronize()
+        dom_ms = e2.elapsed_time(e3) / steps
+        achieved = step_flops / (dom_ms * 1e-3) / 1e12
+        log(f"int8 product alone: {dom_ms * 1e3:.3f} us per launch (h {h0.rows}x{h0.cols})")
+        dom_desc = {"int8_ops_per_launch": step_flops, "us_per_launch": round(dom_ms * 1e3, 3),
+                    "bf16_peak_fraction": round(achieved / BF16_PEAK_TFLOPS, 4)}
     else:
         achieved = value
         dom_desc = {"algorithmic_bytes_per_launch": step_bytes if kind != "gemm" else None,

@@ -24,7 +24,8 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
-HIP_SOURCES = ["gemv.hip", "gemv_mfma.hip", "gemm.hip", "misc.hip", "writer.hip", "qmv_api.cpp"]
+HIP_SOURCES = ["gemv.hip", "gemv_mfma.hip", "gemm.hip", "gemm_i8.hip", "misc.hip", "writer.hip",
+               "qmv_api.cpp"]
 HOST_SOURCES = ["qmv_host.cpp"]  # no HIP: plain g++
 
 

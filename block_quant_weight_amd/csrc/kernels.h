@@ -41,6 +41,13 @@ size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
                        uint32_t batch, float* workspace, hipStream_t stream);
 
+// Product on Q8_0-quantized activations on the int8 matrix cores:
+// y[t][r] = sum_b fl(dw[r,b] dx[t,b]) * s[t,r,b] with exact int32 block
+// sums s of the weight codes and xq (int8 [batch][cols]), dx float32
+// [batch][cols/32].  hipErrorNotSupported when an offset would pass 32 bits.
+hipError_t launch_gemm_q8act(const MatView& m, const int8_t* xq, const float* dx, float* y,
+                             uint32_t batch, hipStream_t stream);
+
 // Batched product on the matrix cores with f16 operands (Q8_0 with f16
 // scales, cols 512 or 1024, any batch): returns hipErrorNotSupported for
 // other matrices, which then take launch_gemm.

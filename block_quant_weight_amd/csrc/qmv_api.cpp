@@ -252,6 +252,18 @@ int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
                                           static_cast<float*>(ws), s));
 }
 
+int qmv_gemm_q8(qmv_handle h, const int8_t* xq, const float* dx, float* y, uint32_t batch,
+                void* stream) {
+    int st = ready(h);
+    if (st != QMV_OK) return st;
+    if (xq == nullptr || dx == nullptr || y == nullptr || batch == 0) return QMV_E_ARG;
+    if (!aligned16(xq) || !aligned16(dx) || !aligned16(y)) return QMV_E_ARG;
+    const hipError_t e = qmv::launch_gemm_q8act(view(h), xq, dx, y, batch,
+                                                static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return QMV_E_SHAPE;
+    return device_status(e);
+}
+
 int qmv_embed_rows(qmv_handle h, const int32_t* ids, uint32_t n, float* out,
                    void* stream) {
     int st = ready(h);

@@ -23,7 +23,7 @@ QMV_E_NOMEM = -5
 EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
-           "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated")
+           "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated", "qmv_gemm_q8")
 
 _lib = None
 
@@ -60,6 +60,7 @@ def lib():
             "qmv_upload_gguf": ([vp, vp, u64, vp], i32),
             "qmv_quantize_weights": ([u32, u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
             "qmv_gemv_gated": ([vp, vp, u32, vp, vp, u32, vp], i32),
+            "qmv_gemm_q8": ([vp, vp, vp, vp, u32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -230,6 +231,18 @@ def qmv_gemv_group(hs, x, ys, batch=None, stream=None):
     _check(lib().qmv_gemv_group(ctypes.cast(harr, ctypes.c_void_p), n, px,
                                 ctypes.cast(yarr, ctypes.c_void_p), b, _stream(stream)),
            "qmv_gemv_group")
+
+
+def qmv_gemm_q8(h: QmvHandle, xq, dx, y, batch=None, stream=None):
+    """Product on Q8_0-quantized activations: xq int8 [batch, cols], dx
+    float32 [batch, cols/32] (from qmv_quantize_q8), y float32 [batch, rows],
+    all on the GPU."""
+    import torch
+    b = xq.shape[0] if (batch is None and xq.dim() == 2) else (batch or 1)
+    pq = _dev(xq, torch.int8, b * h.cols, "xq")
+    pd = _dev(dx, torch.float32, b * (h.cols // 32), "dx")
+    py = _dev(y, torch.float32, b * h.rows, "y")
+    _check(lib().qmv_gemm_q8(h.ptr, pq, pd, py, b, _stream(stream)), "qmv_gemm_q8")
 
 
 ACT_SILU = 0

@@ -231,6 +231,23 @@ int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
              void *stream);
 
 /*
+ * Prefill product on Q8_0-quantized activations (the page's CPU path: the
+ * activations quantized per block of 32 by the "Quantization rule", e.g.
+ * with qmv_quantize_q8, then per-block integer dot products):
+ *   y[t][r] = sum_b fl(dw[r,b] * dx[t,b]) * s[t,r,b],
+ *   s[t,r,b] = sum_j v[r,32b+j] * xq[t,32b+j]   (exact 32-bit integers),
+ * dw the matrix's block scales, v its codes (Q8_0 quants, Q4_0 nibble - 8).
+ * The block sums run on the int8 matrix cores (one 32x32x32 product per
+ * block), the combine is float32: within (cols/32 + 1) * 2^-24 *
+ * sum_b |dw dx s| of the exact sum.  xq: int8 [batch][cols], dx: float32
+ * [batch][cols/32], y: float32 [batch][rows], device memory, 16-byte
+ * aligned.  Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no
+ * upload), QMV_E_SHAPE (an operand of 4 GiB or more), QMV_E_DEVICE.
+ */
+int qmv_gemm_q8(qmv_handle h, const int8_t *xq, const float *dx, float *y, uint32_t batch,
+                void *stream);
+
+/*
  * Embedding-row gather: out[i][c] = fl32(v * d) of row ids[i], bit for bit
  * the dequantized weight (scaling such as an embedding factor is the
  * caller's).  ids: int32 [n], out: float32 [n][cols], device memory.  An id
