@@ -27,6 +27,10 @@ HIP_FLAGS = [
 HIP_SOURCES = ["gemv.hip", "gemv_mfma.hip", "gemm.hip", "gemm_i8.hip", "misc.hip", "writer.hip",
                "qmv_api.cpp"]
 HOST_SOURCES = ["qmv_host.cpp"]  # no HIP: plain g++
+# Per-file flags.  The int8 product reads every matrix-core result with
+# vector instructions; in the accumulation-register form each result would
+# first be copied out (one extra instruction per output per block).
+FILE_FLAGS = {"gemm_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -41,7 +45,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        cmd = ["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ["hipcc", *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd = ["hipcc", *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         jobs.append((obj, cmd))
