@@ -303,7 +303,8 @@ def gated_within_tolerance(h, href, y1, n1, y3, n3, act, rel: float = 2e-3):
     multiply, with L = max |act'|.  Returns (ok, worst ratio err / bound)."""
     h = np.asarray(h, dtype=np.float64)
     e1, e3 = rel * n1, rel * n3
-    a1 = np.abs(np.vectorize(lambda v: ffn_act(v, act))(y1)) if y1.size else y1
+    with np.errstate(over="ignore"):   # e^-a overflows to inf for the far tail: act -> 0
+        a1 = np.abs(np.vectorize(lambda v: ffn_act(v, act))(y1)) if y1.size else y1
     L = ACT_LIPSCHITZ
     bound = L * e1 * (np.abs(y3) + e3) + a1 * e3
     bound = bound + 2.0 ** -20 * (a1 + L * e1) * (np.abs(y3) + e3)
