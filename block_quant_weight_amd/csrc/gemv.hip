@@ -28,14 +28,18 @@ namespace {
 
 constexpr int kWaves = 4;  // wavefronts per workgroup
 
-// Launch-shape override from the environment, for tuning sweeps (the default
-// applies when the variable is unset or not a positive number).
-uint32_t tune_knob(const char* name, uint32_t dflt) {
+// Launch-shape overrides from the environment, for tuning sweeps: each is
+// read once per process (0 when unset or not a positive number, and then
+// the default applies).
+uint32_t env_knob(const char* name) {
     const char* v = getenv(name);
-    if (v == nullptr) return dflt;
+    if (v == nullptr) return 0;
     const long n = strtol(v, nullptr, 10);
-    return n > 0 ? static_cast<uint32_t>(n) : dflt;
+    return n > 0 ? static_cast<uint32_t>(n) : 0;
 }
+uint32_t or_default(uint32_t v, uint32_t dflt) { return v != 0 ? v : dflt; }
+#define QMV_KNOB(NAME, DFLT) \
+    or_default([] { static const uint32_t v = env_knob(NAME); return v; }(), (DFLT))
 
 // Q4_0 block: sum of nibble_j * x_j.  Byte 4i+k gives element 4i+k (low
 // nibble) and element 16+4i+k (high nibble).
@@ -1021,13 +1025,13 @@ hipError_t stream_launch(const MatView* ms, uint32_t n, const float* x, float* c
     for (uint32_t i = n + 1; i <= static_cast<uint32_t>(kMaxGroup); ++i) g.first[i] = 0x7FFFFFFFu;
     const uint32_t cols = ms[0].cols;
     const uint32_t want = (tiles + kStreamWaves - 1) / kStreamWaves;
-    const uint32_t cap = tune_knob("QMV_STREAM_WG", 256);
+    const uint32_t cap = QMV_KNOB("QMV_STREAM_WG", 256);
     const uint32_t blocks = want < cap ? want : cap;
     // QMV_STREAM_ORDER=1: contiguous tile ranges per workgroup
-    const uint32_t per_wg = tune_knob("QMV_STREAM_ORDER", 1) == 1 ? (tiles + blocks - 1) / blocks : 0;
+    const uint32_t per_wg = QMV_KNOB("QMV_STREAM_ORDER", 1) == 1 ? (tiles + blocks - 1) / blocks : 0;
     const size_t lds = static_cast<size_t>(gemv_lds_bytes<WT>(cols, NB));
     const float* xp = x + static_cast<uint64_t>(done) * cols;
-    if (tune_knob("QMV_STREAM_DEPTH", 2) == 3)
+    if (QMV_KNOB("QMV_STREAM_DEPTH", 2) == 3)
         hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 3>), dim3(blocks),
                            dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
     else
@@ -1055,7 +1059,7 @@ bool use_stream(const MatView* ms, uint32_t n) {
     if (nr != 2) return false;
     uint64_t tiles = 0;
     for (uint32_t i = 0; i < n; ++i) tiles += (ms[i].rows + nr - 1) / nr;
-    return tiles >= tune_knob("QMV_STREAM_MIN", 6144);
+    return tiles >= QMV_KNOB("QMV_STREAM_MIN", 6144);
 }
 
 // One streaming launch for a single activation vector (the decode case).
@@ -1081,7 +1085,7 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
     const uint32_t S = (m.cols / CW + 63) / 64;
     uint32_t nr = S == 1 ? 4 : S == 2 ? 2 : 1;
     while (nr > 1 && m.rows / nr < 2048) nr /= 2;
-    nr = tune_knob("QMV_GEMV_NR", nr);
+    nr = QMV_KNOB("QMV_GEMV_NR", nr);
     if (oneshot_fits<WT>(m.cols, NB, nr)) {
         const size_t l = static_cast<size_t>(gemv_lds_bytes<WT>(m.cols, NB));
 #define QMV_ONESHOT(NR_, SMAX_, W_) \
@@ -1260,7 +1264,7 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
         }
         return hipSuccess;
     }
-    const uint32_t nr_want = tune_knob("QMV_GROUP_NR", 1);
+    const uint32_t nr_want = QMV_KNOB("QMV_GROUP_NR", 1);
     const uint32_t nr = (S4 <= 2 && nr_want == 2) ? 2 : 1;  // the NR = 2 kernel has SMAX4 = 2
     uint32_t done = 0;
     while (done < batch) {
