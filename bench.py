@@ -129,7 +129,7 @@ DOMINANT_KERNEL = {
     "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm.hip"),
     "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
     "gemm_q8act_q4_14336x4096": ("gemm_q8act_kernel", "gemm_i8.hip"),
-    "gemm_q8act_q8_4096x14336": ("gemm_q8act_kernel", "gemm_i8.hip"),
+    "gemm_q8act_q8_4096x14336": ("gemm_q8act_kernel + splitk_reduce_kernel", "gemm_i8.hip"),
     "embed_64": ("embed_kernel", "misc.hip"),
     "writer_q4_14336x4096": ("quantize_q4_round_kernel", "writer.hip"),
     "writer_q4_search_14336x4096": ("quantize_q4_search_kernel", "writer.hip"),

@@ -576,6 +576,20 @@ BigPlan big_plan(const MatView& m, uint32_t batch, bool x_f32) {
 
 }  // namespace
 
+hipError_t launch_splitk_sum(const float* part, float* y, uint64_t total, uint32_t splits,
+                             hipStream_t s) {
+    const bool vec = total % 4 == 0;
+    const uint64_t blocks = ((vec ? total / 4 : total) + 255) / 256;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (vec)
+        hipLaunchKernelGGL(big::splitk_reduce_kernel<true>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(256), 0, s, part, y, total, splits);
+    else
+        hipLaunchKernelGGL(big::splitk_reduce_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
+                           dim3(256), 0, s, part, y, total, splits);
+    return hipGetLastError();
+}
+
 size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32) {
     const BigPlan p = big_plan(m, batch, x_f32);
     if (!p.use || p.splits == 1) return 0;
@@ -608,17 +622,7 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.splits == 1) return e;
-        const uint64_t total = static_cast<uint64_t>(batch) * m.rows;
-        const bool vec = total % 4 == 0;
-        const uint64_t blocks = ((vec ? total / 4 : total) + 255) / 256;
-        if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-        if (vec)
-            hipLaunchKernelGGL(big::splitk_reduce_kernel<true>, dim3(static_cast<uint32_t>(blocks)),
-                               dim3(256), 0, s, part, y, total, p.splits);
-        else
-            hipLaunchKernelGGL(big::splitk_reduce_kernel<false>, dim3(static_cast<uint32_t>(blocks)),
-                               dim3(256), 0, s, part, y, total, p.splits);
-        return hipGetLastError();
+        return launch_splitk_sum(part, y, static_cast<uint64_t>(batch) * m.rows, p.splits, s);
     }
     // grid.y carries the token tiles: at most 65535 of them
     if ((batch + 63) / 64 > 65535u) return hipErrorInvalidValue;

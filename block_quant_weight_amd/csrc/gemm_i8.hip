@@ -12,9 +12,10 @@
 // (one conversion, one scale product and one multiply-add per output per
 // block: the vector units, not the matrix cores, set the pace).
 //
-// Work split: a workgroup of 4 waves owns BM tokens (128, or 64 when that
-// gives too few workgroups to fill the chip) x 128 weight rows and walks K
-// in steps of two blocks.  Each step's activation quants, weight
+// Work split: a workgroup of 4 waves owns BM tokens (128, or 64 for batches
+// of at most 64) x 128 weight rows and walks its slice of K in steps of two
+// blocks; when the tiles alone leave compute units idle, K is split into
+// slices whose partial sums a second kernel adds in slice order.  Each step's activation quants, weight
 // codes (Q4_0 nibbles turned into signed bytes n - 8 on the way: byte j of
 // a block gives element j from its low nibble and j + 16 from its high one)
 // and both scale sets go through registers into a double-buffered LDS, one
@@ -63,7 +64,8 @@ __device__ __forceinline__ uint32_t nib_to_i8(uint32_t u) {
 template <uint32_t WT, bool SF16, int BM, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ d, const int8_t* __restrict__ xq,
-    const float* __restrict__ dx, float* __restrict__ y, uint32_t M, uint32_t N, uint32_t K) {
+    const float* __restrict__ dx, float* __restrict__ y, uint32_t M, uint32_t N, uint32_t K,
+    uint32_t k_per_split) {
     constexpr int TI = BM / (16 * NW);  // token tiles of 32 per wave
     __shared__ __attribute__((aligned(16))) uint8_t Xs[2][BM * PITCH];
     __shared__ __attribute__((aligned(16))) uint8_t Ws[2][BN * PITCH];
@@ -74,6 +76,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
     const int wm = wid >> 1, wn = wid & 1;
     const uint32_t m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const uint32_t nb = K >> 5;
+    // this workgroup's slice of K: blocks [kb / 32, ke / 32)
+    const uint32_t kb = blockIdx.z * k_per_split, ke = min(K, kb + k_per_split);
+    const uint32_t nbe = ke >> 5;
     const uint32_t row_bytes = (WT == kQ4) ? (K >> 1) : K;
     const __amdgpu_buffer_rsrc_t xr = rsrc(xq, static_cast<uint64_t>(M) * K);
     const __amdgpu_buffer_rsrc_t sr = rsrc(dx, static_cast<uint64_t>(M) * nb * 4);
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
 
     auto fetch = [&](uint32_t k0, I8Stage& st) {
         const uint32_t b = (k0 >> 5) + half;   // block index within the row
-        const bool kin = b < nb;
+        const bool kin = b < nbe;
         const bool tin = doX && kin && (BM == 128 || slot < BM) && tok < M;
         const bool rin = doW && kin && row < N;
         const uint32_t xo = tin ? tok * K + 32 * b : kOob;
@@ -178,12 +183,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
     };
 
     I8Stage sa, sb;
-    fetch(0, sa);
+    fetch(kb, sa);
     store(sa, 0);
-    fetch(BK, sb);
+    fetch(kb + BK, sb);
     __syncthreads();
     int cur = 0;
-    for (uint32_t k0 = 0; k0 < K; k0 += BK) {
+    for (uint32_t k0 = kb; k0 < ke; k0 += BK) {
         compute(cur);
         // the next step's data into the other buffer, the one after into sa
         store(sb, cur ^ 1);
@@ -192,7 +197,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
         cur ^= 1;
     }
 
-    // lane: weight row n = 32 j + lane % 32, tokens 8 (v / 4) + 4 h + v % 4
+    // lane: weight row n = 32 j + lane % 32, tokens 8 (v / 4) + 4 h + v % 4;
+    // slice z's partial sums go to y + z M N
+    y += static_cast<uint64_t>(blockIdx.z) * M * N;
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -207,39 +214,74 @@ __global__ __launch_bounds__(NW * 64) void gemm_q8act_kernel(
 }
 
 template <int BM, int NW>
-hipError_t q8act_launch(const MatView& m, const int8_t* xq, const float* dx, float* y,
-                        uint32_t batch, hipStream_t s) {
+hipError_t q8act_launch(const MatView& m, const int8_t* xq, const float* dx, float* out,
+                        uint32_t batch, uint32_t splits, uint32_t k_per_split, hipStream_t s) {
     const uint32_t gm = (batch + BM - 1) / BM;
-    if (gm > 65535u) return hipErrorInvalidValue;
-    const dim3 grid((m.rows + BN - 1) / BN, gm), block(NW * 64);
+    if (gm > 65535u || splits > 65535u) return hipErrorInvalidValue;
+    const dim3 grid((m.rows + BN - 1) / BN, gm, splits), block(NW * 64);
     if (m.wtype == kQ4) {
         if (m.scale_f16)
-            hipLaunchKernelGGL((gemm_q8act_kernel<kQ4, true, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, y, batch, m.rows, m.cols);
+            hipLaunchKernelGGL((gemm_q8act_kernel<kQ4, true, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, out, batch, m.rows, m.cols, k_per_split);
         else
-            hipLaunchKernelGGL((gemm_q8act_kernel<kQ4, false, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, y, batch, m.rows, m.cols);
+            hipLaunchKernelGGL((gemm_q8act_kernel<kQ4, false, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, out, batch, m.rows, m.cols, k_per_split);
     } else {
         if (m.scale_f16)
-            hipLaunchKernelGGL((gemm_q8act_kernel<kQ8, true, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, y, batch, m.rows, m.cols);
+            hipLaunchKernelGGL((gemm_q8act_kernel<kQ8, true, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, out, batch, m.rows, m.cols, k_per_split);
         else
-            hipLaunchKernelGGL((gemm_q8act_kernel<kQ8, false, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, y, batch, m.rows, m.cols);
+            hipLaunchKernelGGL((gemm_q8act_kernel<kQ8, false, BM, NW>), grid, block, 0, s, m.q, m.d, xq, dx, out, batch, m.rows, m.cols, k_per_split);
     }
     return hipGetLastError();
 }
 
-}  // namespace
+// Launch shape: token tile, and the K slices.  Tiles of 128 tokens (64 for
+// batches of at most 64); while there are fewer than 384 workgroups (1.5 per
+// compute unit) and each slice keeps at least 8 steps, K is split in two
+// again.
+struct Q8Plan {
+    bool small = false;
+    uint32_t splits = 1, k_per_split = 0;
+};
 
-hipError_t launch_gemm_q8act(const MatView& m, const int8_t* xq, const float* dx, float* y,
-                             uint32_t batch, hipStream_t s) {
+Q8Plan q8_plan(const MatView& m, uint32_t batch) {
+    Q8Plan p;
+    p.small = batch <= 64;
+    const uint32_t bm = p.small ? 64 : 128;
+    const uint64_t tiles = uint64_t{(m.rows + BN - 1) / BN} * ((batch + bm - 1) / bm);
+    const uint32_t steps = (m.cols + BK - 1) / BK;
+    uint32_t splits = 1;
+    while (tiles * splits < 384 && steps / (2 * splits) >= 8) splits *= 2;
+    const uint32_t per = (steps + splits - 1) / splits;
+    p.k_per_split = per * BK;
+    p.splits = (m.cols + p.k_per_split - 1) / p.k_per_split;
+    return p;
+}
+
+bool q8act_fits(const MatView& m, uint32_t batch) {
     // 32-bit buffer offsets over the activations, their scales, the codes
     // and the weight scales
     const uint64_t qbytes = (m.wtype == kQ4) ? uint64_t{m.rows} * m.cols / 2 : uint64_t{m.rows} * m.cols;
-    if (uint64_t{batch} * m.cols >= 0xFFFFFFF0ull || qbytes >= 0xFFFFFFF0ull ||
-        uint64_t{m.rows} * (m.cols / 32) * 4 >= 0xFFFFFFF0ull)
-        return hipErrorNotSupported;
-    // 64-token tiles when 128-token ones leave compute units idle
-    const uint64_t tiles128 = uint64_t{(m.rows + BN - 1) / BN} * ((batch + 127) / 128);
-    if (tiles128 < 256) return q8act_launch<64, 4>(m, xq, dx, y, batch, s);
-    return q8act_launch<128, 4>(m, xq, dx, y, batch, s);
+    return uint64_t{batch} * m.cols < 0xFFFFFFF0ull && qbytes < 0xFFFFFFF0ull &&
+           uint64_t{m.rows} * (m.cols / 32) * 4 < 0xFFFFFFF0ull;
+}
+
+}  // namespace
+
+size_t gemm_q8act_workspace_bytes(const MatView& m, uint32_t batch) {
+    if (!q8act_fits(m, batch)) return 0;
+    const Q8Plan p = q8_plan(m, batch);
+    return p.splits > 1 ? static_cast<size_t>(p.splits) * batch * m.rows * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_q8act(const MatView& m, const int8_t* xq, const float* dx, float* y,
+                             uint32_t batch, float* workspace, hipStream_t s) {
+    if (!q8act_fits(m, batch)) return hipErrorNotSupported;
+    const Q8Plan p = q8_plan(m, batch);
+    float* out = p.splits > 1 ? workspace : y;
+    if (out == nullptr) return hipErrorInvalidValue;
+    const hipError_t e = p.small ? q8act_launch<64, 4>(m, xq, dx, out, batch, p.splits, p.k_per_split, s)
+                                 : q8act_launch<128, 4>(m, xq, dx, out, batch, p.splits, p.k_per_split, s);
+    if (e != hipSuccess || p.splits == 1) return e;
+    return launch_splitk_sum(workspace, y, uint64_t{batch} * m.rows, p.splits, s);
 }
 
 }  // namespace qmv

@@ -41,12 +41,19 @@ size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
                        uint32_t batch, float* workspace, hipStream_t stream);
 
+// y[i] = sum over z < splits of part[z * total + i], added in z order.
+hipError_t launch_splitk_sum(const float* part, float* y, uint64_t total, uint32_t splits,
+                             hipStream_t stream);
+
 // Product on Q8_0-quantized activations on the int8 matrix cores:
 // y[t][r] = sum_b fl(dw[r,b] dx[t,b]) * s[t,r,b] with exact int32 block
 // sums s of the weight codes and xq (int8 [batch][cols]), dx float32
-// [batch][cols/32].  hipErrorNotSupported when an offset would pass 32 bits.
+// [batch][cols/32].  K may be split as in launch_gemm (workspace of
+// gemm_q8act_workspace_bytes).  hipErrorNotSupported when an offset would
+// pass 32 bits.
+size_t gemm_q8act_workspace_bytes(const MatView& m, uint32_t batch);
 hipError_t launch_gemm_q8act(const MatView& m, const int8_t* xq, const float* dx, float* y,
-                             uint32_t batch, hipStream_t stream);
+                             uint32_t batch, float* workspace, hipStream_t stream);
 
 // Batched product on the matrix cores with f16 operands (Q8_0 with f16
 // scales, cols 512 or 1024, any batch): returns hipErrorNotSupported for

@@ -258,8 +258,12 @@ int qmv_gemm_q8(qmv_handle h, const int8_t* xq, const float* dx, float* y, uint3
     if (st != QMV_OK) return st;
     if (xq == nullptr || dx == nullptr || y == nullptr || batch == 0) return QMV_E_ARG;
     if (!aligned16(xq) || !aligned16(dx) || !aligned16(y)) return QMV_E_ARG;
-    const hipError_t e = qmv::launch_gemm_q8act(view(h), xq, dx, y, batch,
-                                                static_cast<hipStream_t>(stream));
+    const qmv::MatView v = view(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = workspace_for(s, qmv::gemm_q8act_workspace_bytes(v, batch), &ws);
+    if (st != QMV_OK) return st;
+    const hipError_t e = qmv::launch_gemm_q8act(v, xq, dx, y, batch, static_cast<float*>(ws), s);
     if (e == hipErrorNotSupported) return QMV_E_SHAPE;
     return device_status(e);
 }

@@ -27,8 +27,8 @@
  *
  * Streams: `stream` is a hipStream_t passed as a pointer; NULL is the null
  * stream.  Compute calls only enqueue work on it and return; they never
- * synchronize.  The one exception to "no allocation": a large-batch
- * qmv_gemm that splits K keeps its partial sums in a workspace owned by the
+ * synchronize.  The one exception to "no allocation": a qmv_gemm or
+ * qmv_gemm_q8 call that splits K keeps its partial sums in a workspace owned by the
  * library, one per (device, stream), allocated on first need and grown (never
  * freed) for a larger batch; that first call on a stream must not be made
  * while the stream is being captured into a graph (QMV_E_ARG).
@@ -241,8 +241,12 @@ int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
  * block), the combine is float32: within (cols/32 + 1) * 2^-24 *
  * sum_b |dw dx s| of the exact sum.  xq: int8 [batch][cols], dx: float32
  * [batch][cols/32], y: float32 [batch][rows], device memory, 16-byte
- * aligned.  Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no
- * upload), QMV_E_SHAPE (an operand of 4 GiB or more), QMV_E_DEVICE.
+ * aligned.  When the output tiles are too few to fill the GPU, K is split
+ * and the slices' partial sums are added in slice order by a second kernel
+ * (deterministic), in a per-stream workspace as for qmv_gemm.  Errors:
+ * QMV_E_ARG (null or misaligned pointer, batch 0, no upload, a first
+ * split-K call on a stream under graph capture), QMV_E_SHAPE (an operand
+ * of 4 GiB or more), QMV_E_NOMEM (workspace), QMV_E_DEVICE.
  */
 int qmv_gemm_q8(qmv_handle h, const int8_t *xq, const float *dx, float *y, uint32_t batch,
                 void *stream);
