@@ -99,3 +99,23 @@ def test_random_q8act(seed):
         assert ok, (wt, sf, R, C, B, worst)
     finally:
         Q.qmv_destroy(h)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_batched_classifier(seed):
+    """Q8_0 with f16 scales, 512 or 1024 columns, batches above 8: the
+    f16 matrix-core path, with rows that end mid-tile and token counts that
+    end mid-pass."""
+    g = np.random.default_rng(7000 + seed)
+    C = int(g.choice([512, 1024]))
+    R = int(g.integers(1, 5000))
+    B = int(g.integers(9, 200))
+    img = K.make_image(500 + seed, 0, K.Q8, 1, R, C)
+    h = K.upload(img, K.Q8, 1, R, C)
+    try:
+        x = K.make_x(500 + seed, 1, B, C)
+        ref, norm = O.product(img, K.Q8, 1, R, C, x, threads=K.THREADS)
+        ok, worst = O.within_tolerance(K.gpu_gemv(h, x), ref, norm)
+        assert ok, (R, C, B, worst)
+    finally:
+        Q.qmv_destroy(h)
