@@ -53,6 +53,9 @@ constexpr int kMaxCols = 1024;  // activations of one pass must fit LDS
 constexpr uint32_t kOob = 0xFFFFFFF0u;
 constexpr int kXBytes = kTokens * (2 * kMaxCols + 16);
 constexpr int kSlice = 32 * 64;  // a wave's LDS slice: 32 rows x one block pair
+// cache-policy bits of the output stores: non-temporal (measured 77.4 ->
+// 72.6-74.7 us for 248320 x 1024 at batch 64, bit-identical)
+constexpr int kStreamStore = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -268,9 +271,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
             for (int e = 0; e < 16; ++e) {
                 const uint32_t t = 32 * mt + 8 * (e / 4) + 4 * h + (e % 4);
                 const uint32_t off = (rok && t < ntok) ? (t * rows + row) * 4 : kOob;
-                // the store takes the 32-bit pattern (an unsigned int)
+                // the store takes the 32-bit pattern (an unsigned int);
+                // non-temporal: the logits are not read again here
                 __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[mt][e] * tinv[t]),
-                                                      yrs, off, 0, 0);
+                                                      yrs, off, 0, kStreamStore);
                 acc[mt][e] = 0.f;
             }
     };
