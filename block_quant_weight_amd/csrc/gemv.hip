@@ -1076,20 +1076,26 @@ hipError_t stream_pass(const MatView* ms, uint32_t n, const float* x, float* con
 }
 
 // Launch shape: S = steps per row (64 chunks each).  Rows per wave NR: up to
-// 4 for S = 1 (a wave's quant loads stay <= 4 per lane), 1 beyond, and never
-// so many that fewer than 2048 waves (8 per compute unit) remain.  Eight
-// waves per workgroup share one LDS copy of the activations for one-step
-// rows, sixteen for longer rows (for two-step rows, one row per wave in
-// sixteen-wave groups measured 3.65 us on Q4_0 4096 x 4096 against 3.77 us
-// for two rows per wave in eight-wave groups, and four-step rows 5.6 us
-// against 6.1 us on Q4_0 4096 x 8192; for one-step rows sixteen-wave groups
-// were slower).  QMV_GEMV_NR overrides NR (tuning sweeps).
+// 4 for S = 1 and 2 for S = 2 (a wave's quant loads stay <= 4 per lane), 1
+// beyond, and never so many that fewer than 2048 waves (8 per compute unit)
+// remain.  Eight waves per workgroup share one LDS copy of the activations,
+// sixteen for rows of more than four steps (fewer copies of a wide vector),
+// and for 4096 to 8192 rows of two to four steps, which then take one row
+// per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
+// 6.1 -> 5.6 us, Q8_0 4096 x 4096 4.77 -> 4.69 us; but 11008 x 4096 Q4_0
+// 7.0 us against 6.6 us with two rows per wave in eight-wave groups, 1024 x
+// 4096 slower too, and one-step rows slower in sixteen-wave groups.
+// QMV_GEMV_NR overrides NR (tuning sweeps).
 template <uint32_t WT, bool SF16, int NB>
 hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) {
     constexpr uint32_t CW = DigitLayout<WT>::CW;
     const uint32_t S = (m.cols / CW + 63) / 64;
-    uint32_t nr = S == 1 ? 4 : 1;
+    uint32_t nr = S == 1 ? 4 : S == 2 ? 2 : 1;
     while (nr > 1 && m.rows / nr < 2048) nr /= 2;
+    // rows of two to four steps, 4096 to 8192 of them: one row per wave in
+    // sixteen-wave groups (one or two groups per compute unit)
+    const bool wide = S >= 2 && S <= 4 && m.rows >= 16 * 256 && m.rows <= 2 * 16 * 256;
+    if (wide) nr = 1;
     nr = QMV_KNOB("QMV_GEMV_NR", nr);
     if (oneshot_fits<WT>(m.cols, NB, nr)) {
         const size_t l = static_cast<size_t>(gemv_lds_bytes<WT>(m.cols, NB));
@@ -1099,8 +1105,12 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
         QMV_ONESHOT(2, 1, 8)
         QMV_ONESHOT(2, 2, 8)
         QMV_ONESHOT(1, 1, 8)
-        QMV_ONESHOT(1, 2, 16)
-        QMV_ONESHOT(1, 4, 16)
+        if (wide) {
+            QMV_ONESHOT(1, 2, 16)
+            QMV_ONESHOT(1, 4, 16)
+        }
+        QMV_ONESHOT(1, 2, 8)
+        QMV_ONESHOT(1, 4, 8)
         QMV_ONESHOT(1, 8, 16)
         QMV_ONESHOT(1, 12, 16)
         QMV_ONESHOT(1, 16, 16)
