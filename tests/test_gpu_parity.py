@@ -85,6 +85,28 @@ def test_gemv_small_full(wt, sf, R, C):
         Q.qmv_destroy(h)
 
 
+# Every one-shot launch shape, full oracle: rows per wave 4 / 2 / 1 for rows
+# of one step (64 chunks of 16 bytes), 2 or 1 for two steps, sixteen-wave
+# groups of one row for 4096-8192 rows of two to four steps (at both ends
+# of that band, ragged), eight-wave groups below it, and rows of more steps.
+SHAPES = [(2, 0, 8200, 1024), (1, 1, 5000, 512), (2, 1, 8500, 4096), (2, 1, 4100, 4096),
+          (1, 0, 8192, 2048), (1, 1, 5000, 4096), (2, 0, 4097, 6144), (2, 1, 1000, 4096),
+          (1, 1, 2000, 4096), (2, 1, 4095, 4096), (1, 0, 8193, 2048)]
+
+
+@pytest.mark.parametrize("wt,sf,R,C", SHAPES)
+def test_gemv_launch_shapes_full(wt, sf, R, C):
+    img = K.make_image(150, R + C, wt, sf, R, C, lo=-1e-2)
+    h = K.upload(img, wt, sf, R, C)
+    try:
+        for batch in (1, 3):
+            x = K.make_x(150, R + batch, batch, C)
+            ref, norm = O.product(img, wt, sf, R, C, x, threads=K.THREADS)
+            close(K.gpu_gemv(h, x), ref, norm, f"gemv {wt}/{sf} {R}x{C} b{batch}")
+    finally:
+        Q.qmv_destroy(h)
+
+
 @pytest.mark.parametrize("wt,sf", [(1, 1), (2, 1), (2, 0)])
 @pytest.mark.parametrize("batch", [9, 16, 33, 64, 65])
 def test_gemv_large_batch_matrix_core_path(wt, sf, batch):
