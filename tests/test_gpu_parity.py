@@ -350,6 +350,28 @@ def test_gemv_group_mixed_types_against_oracle_and_single():
             Q.qmv_destroy(h)
 
 
+@pytest.mark.parametrize("wt,sf,R,C", [(2, 1, 6200, 4096), (2, 0, 6201, 4096),
+                                       (1, 0, 6144, 2048), (1, 1, 6145, 2048)])
+def test_gemv_group_streaming_kernel_full(wt, sf, R, C):
+    """Two same-type matrices of two-step rows with at least 6144 row pairs
+    between them: the one-workgroup-per-compute-unit streaming kernel at
+    batch 1 (odd row counts end in a half tile), full oracle."""
+    import torch
+    imgs = [K.make_image(820, m, wt, sf, R, C, lo=-1e-2) for m in range(2)]
+    hs = [K.upload(img, wt, sf, R, C) for img in imgs]
+    try:
+        x = K.make_x(820, 5, 1, C)
+        ys = [torch.empty((1, R), dtype=torch.float32, device="cuda") for _ in hs]
+        Q.qmv_gemv_group(hs, K.dev(x), ys)
+        torch.cuda.synchronize()
+        for img, h, y in zip(imgs, hs, ys):
+            ref, norm = O.product(img, wt, sf, R, C, x, threads=K.THREADS)
+            close(y.cpu().numpy(), ref, norm, f"stream {wt}/{sf} {R}x{C}")
+    finally:
+        for h in hs:
+            Q.qmv_destroy(h)
+
+
 def test_gemv_group_rejects_mismatched_cols():
     import torch
     a = K.upload(K.make_image(801, 0, 2, 1, 64, 128), 2, 1, 64, 128)
