@@ -1078,10 +1078,11 @@ hipError_t stream_pass(const MatView* ms, uint32_t n, const float* x, float* con
 // Launch shape: S = steps per row (64 chunks each).  Rows per wave NR: up to
 // 4 for S = 1 and 2 for S = 2 (a wave's quant loads stay <= 4 per lane), 1
 // beyond, and never so many that fewer than 2048 waves (8 per compute unit)
-// remain.  Eight waves per workgroup share one LDS copy of the activations,
-// sixteen for rows of more than four steps (fewer copies of a wide vector),
-// and for 4096 to 8192 rows of two to four steps, which then take one row
-// per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
+// remain.  Four waves per workgroup share one LDS copy of the activations
+// for one-step rows (the LM head 248320 x 1024 Q8_0: 40.2 -> 39.0 us against
+// eight), eight for longer rows, sixteen for rows of more than four steps
+// (fewer copies of a wide vector) and for 4096 to 8192 rows of two to four
+// steps, which then take one row per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
 // 6.1 -> 5.6 us, Q8_0 4096 x 4096 4.77 -> 4.69 us; but 11008 x 4096 Q4_0
 // 7.0 us against 6.6 us with two rows per wave in eight-wave groups, 1024 x
 // 4096 slower too, and one-step rows slower in sixteen-wave groups.
@@ -1101,10 +1102,10 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
         const size_t l = static_cast<size_t>(gemv_lds_bytes<WT>(m.cols, NB));
 #define QMV_ONESHOT(NR_, SMAX_, W_) \
     if (nr == NR_ && S <= SMAX_) return gemv_oneshot_launch<WT, SF16, NR_, NB, SMAX_, W_>(m, x, y, l, s);
-        QMV_ONESHOT(4, 1, 8)
-        QMV_ONESHOT(2, 1, 8)
+        QMV_ONESHOT(4, 1, 4)
+        QMV_ONESHOT(2, 1, 4)
         QMV_ONESHOT(2, 2, 8)
-        QMV_ONESHOT(1, 1, 8)
+        QMV_ONESHOT(1, 1, 4)
         if (wide) {
             QMV_ONESHOT(1, 2, 16)
             QMV_ONESHOT(1, 4, 16)
