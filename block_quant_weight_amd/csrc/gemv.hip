@@ -1080,9 +1080,10 @@ hipError_t stream_pass(const MatView* ms, uint32_t n, const float* x, float* con
 // beyond, and never so many that fewer than 2048 waves (8 per compute unit)
 // remain.  Four waves per workgroup share one LDS copy of the activations
 // for one-step rows (the LM head 248320 x 1024 Q8_0: 40.2 -> 39.0 us against
-// eight), eight for longer rows, sixteen for rows of more than four steps
-// (fewer copies of a wide vector) and for 4096 to 8192 rows of two to four
-// steps, which then take one row per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
+// eight) and for fewer than 4096 rows of two to four steps (1024 x 4096:
+// 2.49 -> 2.39 us), eight for other rows of up to four steps, sixteen for
+// rows of more than four steps (fewer copies of a wide vector) and for 4096
+// to 8192 rows of two to four steps, which then take one row per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
 // 6.1 -> 5.6 us, Q8_0 4096 x 4096 4.77 -> 4.69 us; but 11008 x 4096 Q4_0
 // 7.0 us against 6.6 us with two rows per wave in eight-wave groups, 1024 x
 // 4096 slower too, and one-step rows slower in sixteen-wave groups.
@@ -1109,6 +1110,10 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
         if (wide) {
             QMV_ONESHOT(1, 2, 16)
             QMV_ONESHOT(1, 4, 16)
+        }
+        if (m.rows < 16 * 256) {  // fewer rows: smaller groups spread them over more compute units
+            QMV_ONESHOT(1, 2, 4)
+            QMV_ONESHOT(1, 4, 4)
         }
         QMV_ONESHOT(1, 2, 8)
         QMV_ONESHOT(1, 4, 8)
