@@ -18,8 +18,6 @@
 // conversion is one v_cvt_f32_ubyteN per weight.  sum_j x_j is accumulated
 // in the same element order as raw, so a block of all-zero weights gives
 // raw == OFF * sum exactly (OFF is a power of two) and contributes exactly 0.
-#include <cstdlib>
-
 #include "device_common.h"
 #include "kernels.h"
 
@@ -27,19 +25,6 @@ namespace qmv {
 namespace {
 
 constexpr int kWaves = 4;  // wavefronts per workgroup
-
-// Launch-shape overrides from the environment, for tuning sweeps: each is
-// read once per process (0 when unset or not a positive number, and then
-// the default applies).
-uint32_t env_knob(const char* name) {
-    const char* v = getenv(name);
-    if (v == nullptr) return 0;
-    const long n = strtol(v, nullptr, 10);
-    return n > 0 ? static_cast<uint32_t>(n) : 0;
-}
-uint32_t or_default(uint32_t v, uint32_t dflt) { return v != 0 ? v : dflt; }
-#define QMV_KNOB(NAME, DFLT) \
-    or_default([] { static const uint32_t v = env_knob(NAME); return v; }(), (DFLT))
 
 // Q4_0 block: sum of nibble_j * x_j.  Byte 4i+k gives element 4i+k (low
 // nibble) and element 16+4i+k (high nibble).
@@ -353,13 +338,25 @@ __device__ __forceinline__ void stage_half(const float4 (&xv)[4], uint32_t h,
                          xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
     // largest magnitude as an integer maximum of the absolute bit patterns,
     // so that inf and NaN win over every finite value
-    uint32_t m = 0;
+    // and the smallest nonzero magnitude (zeros count as the largest pattern)
+    uint32_t m = 0, mn = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu;
+        m = max(m, b);
+        mn = min(mn, b - 1u);  // 0 wraps to the largest pattern
+    }
     m = max(m, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(m))));
+    mn = min(mn, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(mn))));
     const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
+    // A block holding a nonzero value below 2^(E-12) would keep that value
+    // to worse than 2^-11 of itself in 24-bit fixed point: such a ("wide")
+    // block is marked by a negative factor and multiplied in float32 from the
+    // activations themselves (mn + 1 is the smallest nonzero magnitude).
+    const bool wide = mn != 0xFFFFFFFFu &&
+                      __builtin_bit_cast(float, mn + 1u) < __builtin_amdgcn_ldexpf(1.0f, E - 12);
     const float sx = m >= 0x7F800000u ? __builtin_bit_cast(float, 0x7FC00000u)
-                                      : __builtin_amdgcn_ldexpf(1.0f, E - 22);
+                                      : __builtin_amdgcn_ldexpf(wide ? -1.0f : 1.0f, E - 22);
     // X + 0x808080 in the low three bytes: rne(x * 2^(22-E)) by adding
     // 1.5 * 2^23, whose bits are then 0x4B400000 + X
     uint32_t u[16];
@@ -402,6 +399,43 @@ __device__ __forceinline__ void stage_half(const float4 (&xv)[4], uint32_t h,
     }
 }
 
+// Float32 sums of one chunk for a wide block: sum_j v_j x_j with the codes
+// v_j as they are (Q4_0: nibble - 8, element j from the low nibble of byte j
+// and element j + 16 from its high nibble; Q8_0: the signed quant), the
+// activations xc[0 .. CW) read again from memory.
+__device__ __forceinline__ float q4_f32_dot(const uint4 w, const float* __restrict__ xc) {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+    const float4* x4 = reinterpret_cast<const float4*>(xc);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 lo = x4[i], hi = x4[4 + i];
+        const float xl[4] = {lo.x, lo.y, lo.z, lo.w}, xh[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = static_cast<int>((q[i] >> (8 * k)) & 0xFFu);
+            acc = fmaf(static_cast<float>((b & 15) - 8), xl[k], acc);
+            acc = fmaf(static_cast<float>((b >> 4) - 8), xh[k], acc);
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float q8_f32_dot(const uint4 w, const float* __restrict__ xc) {
+    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+    const float4* x4 = reinterpret_cast<const float4*>(xc);
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 xv = x4[i];
+        const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            acc = fmaf(static_cast<float>(static_cast<int8_t>((q[i] >> (8 * k)) & 0xFFu)), xs[k], acc);
+    }
+    return acc;
+}
+
 // T0 + 256 T1 + 65536 T2 in float32 (T1 + 256 T2 is exact in int32).
 __device__ __forceinline__ float combine_digits(int t0, int t1, int t2) {
     const int hi = t1 + t2 * 256;
@@ -441,6 +475,45 @@ __device__ __forceinline__ float q8_digit_dot(const uint4 w, const int4 (&pc)[3]
         t[dd] = a;
     }
     return combine_digits(t[0], t[1], t[2]);
+}
+
+// Adds one chunk of every row (quants qv[r][k], scale bits dv[r][k]) times
+// the staged activations of one vector (digit pieces pc, block info at
+// slot `is` of `info`) to acc[r], where `valid`.  A wide block (negative
+// factor) is multiplied in float32 from xc, its activations in memory.
+template <uint32_t WT, bool SF16, int NR, int SMAX>
+__device__ __forceinline__ void chunk_rows(const uint4 (&qv)[NR][SMAX], const uint32_t (&dv)[NR][SMAX],
+                                           int k, const int4 (&pc)[DigitLayout<WT>::P],
+                                           const uint8_t* __restrict__ info, uint32_t is,
+                                           const float* __restrict__ xc, bool valid,
+                                           float (&acc)[NR]) {
+    float t[NR], f[NR];
+    float sx;
+    if constexpr (WT == kQ4) {
+        const int4 in = reinterpret_cast<const int4*>(info)[is];
+        sx = __builtin_bit_cast(float, in.w);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) t[r] = q4_digit_dot(qv[r][k], pc, in);
+    } else {
+        sx = reinterpret_cast<const float*>(info)[is];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) t[r] = q8_digit_dot(qv[r][k], pc);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) f[r] = scale_from_bits<SF16>(dv[r][k]) * sx;
+    // (only for chunks inside the row: past its end the slot is never written)
+    if (__builtin_expect(valid && sx < 0.f, 0)) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            t[r] = WT == kQ4 ? q4_f32_dot(qv[r][k], xc) : q8_f32_dot(qv[r][k], xc);
+            f[r] = scale_from_bits<SF16>(dv[r][k]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float a = fmaf(f[r], t[r], acc[r]);
+        acc[r] = valid ? a : acc[r];
+    }
 }
 
 // Half blocks of activations each thread loads before the quants: enough for
@@ -563,24 +636,9 @@ __device__ __forceinline__ void oneshot_body(
                 int4 pc[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
-                if constexpr (WT == kQ4) {
-                    const int4 info = reinterpret_cast<const int4*>(base + dig_bytes)[k * 64 + lane];
-                    const float sx = __builtin_bit_cast(float, info.w);
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const float t = q4_digit_dot(qv[r][k], pc, info);
-                        const float a = fmaf(scale_from_bits<SF16>(dv[r][k]) * sx, t, acc[b][r]);
-                        acc[b][r] = valid ? a : acc[b][r];
-                    }
-                } else {
-                    const float sx = reinterpret_cast<const float*>(base + dig_bytes)[k * 64 + lane];
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const float t = q8_digit_dot(qv[r][k], pc);
-                        const float a = fmaf(scale_from_bits<SF16>(dv[r][k]) * sx, t, acc[b][r]);
-                        acc[b][r] = valid ? a : acc[b][r];
-                    }
-                }
+                const float* xc = x + static_cast<uint64_t>(b) * cols + (lane + 64u * k) * CW;
+                chunk_rows<WT, SF16, NR>(qv, dv, k, pc, base + dig_bytes, k * 64 + lane, xc, valid,
+                                         acc[b]);
             }
         }
     }
@@ -606,12 +664,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_oneshot_kernel(
 // Streaming kernel for large matrices: one workgroup of 8 waves per compute
 // unit (measured 10.4-10.7 us for w1 | w3, 2 x 11008 x 4096 Q4_0, against
 // 11.0-11.6 us with 16 waves, 10.8 us with 12 and 12.1 us with 4) converts
-// the activations once, then each wave walks over row tiles
-// (NR rows each) t = w, w + W, w + 2W, ... of a list of matrices of one
-// storage type, with the loads of its next two tiles in flight while it
-// multiplies the current one.  The tile loop is branch-free around the
+// the activations once, then each wave walks over a contiguous range of row
+// tiles (NR rows each) of a list of matrices of one storage type, with the
+// loads of its next tile in flight while it multiplies the current one (a
+// three-deep ring measured slower).  The tile loop is branch-free around the
 // loads: a tile past the end gets an empty buffer range, so its loads return
-// zeros without memory traffic and the three register sets rotate in
+// zeros without memory traffic and the two register sets alternate in
 // straight-line code (loads complete in issue order, so each wait covers one
 // tile only).
 // ---------------------------------------------------------------------------
@@ -754,7 +812,8 @@ __device__ __forceinline__ float ffn_act(float a, uint32_t act) {
 // Gated (GATED = true): stores act(w1 row) * (w3 row) for each row pair.
 template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED>
 __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<NR, SMAX>& b,
-                                             const uint8_t* __restrict__ lds, uint32_t cols,
+                                             const uint8_t* __restrict__ lds,
+                                             const float* __restrict__ x, uint32_t cols,
                                              uint32_t S, uint32_t lane, uint32_t act) {
     using L = DigitLayout<WT>;
     constexpr int P = L::P;
@@ -777,24 +836,9 @@ __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<N
                 int4 pc[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
-                if constexpr (WT == kQ4) {
-                    const int4 info = reinterpret_cast<const int4*>(base + dig_bytes)[k * 64 + lane];
-                    const float sx = __builtin_bit_cast(float, info.w);
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const float t = q4_digit_dot(b.q[r][k], pc, info);
-                        const float a = fmaf(scale_from_bits<SF16>(b.d[r][k]) * sx, t, acc[v][r]);
-                        acc[v][r] = valid ? a : acc[v][r];
-                    }
-                } else {
-                    const float sx = reinterpret_cast<const float*>(base + dig_bytes)[k * 64 + lane];
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const float t = q8_digit_dot(b.q[r][k], pc);
-                        const float a = fmaf(scale_from_bits<SF16>(b.d[r][k]) * sx, t, acc[v][r]);
-                        acc[v][r] = valid ? a : acc[v][r];
-                    }
-                }
+                const float* xc = x + static_cast<uint64_t>(v) * cols + (lane + 64u * k) * L::CW;
+                chunk_rows<WT, SF16, NR>(b.q, b.d, k, pc, base + dig_bytes, k * 64 + lane, xc, valid,
+                                         acc[v]);
             }
         }
     }
@@ -823,7 +867,7 @@ __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<N
     }
 }
 
-template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int DEPTH, bool GATED = false>
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED = false>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     TileArgs g, const float* __restrict__ x, uint32_t cols, uint32_t per_wg, uint32_t act) {
     extern __shared__ float4 smem[];
@@ -868,13 +912,12 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     uint32_t mat = 0;
     // tiles at or past `end` load nothing
     auto tile = [&](uint32_t u) { return u < end ? u : 0xFFFFFFFEu; };
-    TileRegs<NR, SMAX> ra, rb, rc;
+    TileRegs<NR, SMAX> ra, rb;
     auto load_any = [&](uint32_t u, TileRegs<NR, SMAX>& regs) {
         if constexpr (GATED) load_tile_gated<WT, SF16, NR, SMAX>(g, u, cols, lane, regs);
         else load_tile<WT, SF16, NR, SMAX>(g, u, cols, lane, mat, regs);
     };
     load_any(tile(t), ra);
-    if constexpr (DEPTH == 3) load_any(tile(t + step), rb);
 
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t v = j / nhalf, h = j - v * nhalf;
@@ -894,33 +937,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     }
     __syncthreads();
 
-    if constexpr (DEPTH == 3) {
-        // three register sets in rotation: the loads of the next two tiles
-        // are in flight while a tile is multiplied
-        while (t < end) {
-            load_any(tile(t + 2 * step), rc);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, cols, S, lane, act);
-            t += step;
-            if (t >= end) break;
-            load_any(tile(t + 2 * step), ra);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, cols, S, lane, act);
-            t += step;
-            if (t >= end) break;
-            load_any(tile(t + 2 * step), rb);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rc, lds, cols, S, lane, act);
-            t += step;
-        }
-    } else {
-        // two register sets: the next tile's loads are in flight
-        while (t < end) {
-            load_any(tile(t + step), rb);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, cols, S, lane, act);
-            t += step;
-            if (t >= end) break;
-            load_any(tile(t + step), ra);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, cols, S, lane, act);
-            t += step;
-        }
+    // two register sets: the next tile's loads are in flight
+    while (t < end) {
+        load_any(tile(t + step), rb);
+        compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, x, cols, S, lane, act);
+        t += step;
+        if (t >= end) break;
+        load_any(tile(t + step), ra);
+        compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, x, cols, S, lane, act);
+        t += step;
     }
 }
 
@@ -1027,18 +1052,14 @@ hipError_t stream_launch(const MatView* ms, uint32_t n, const float* x, float* c
     for (uint32_t i = n + 1; i <= static_cast<uint32_t>(kMaxGroup); ++i) g.first[i] = 0x7FFFFFFFu;
     const uint32_t cols = ms[0].cols;
     const uint32_t want = (tiles + kStreamWaves - 1) / kStreamWaves;
-    const uint32_t cap = QMV_KNOB("QMV_STREAM_WG", 256);
+    const uint32_t cap = 256;
     const uint32_t blocks = want < cap ? want : cap;
-    // QMV_STREAM_ORDER=1: contiguous tile ranges per workgroup
-    const uint32_t per_wg = QMV_KNOB("QMV_STREAM_ORDER", 1) == 1 ? (tiles + blocks - 1) / blocks : 0;
+    // contiguous tile ranges per workgroup
+    const uint32_t per_wg = (tiles + blocks - 1) / blocks;
     const size_t lds = static_cast<size_t>(gemv_lds_bytes<WT>(cols, NB));
     const float* xp = x + static_cast<uint64_t>(done) * cols;
-    if (QMV_KNOB("QMV_STREAM_DEPTH", 2) == 3)
-        hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 3>), dim3(blocks),
-                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
-    else
-        hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 2>), dim3(blocks),
-                           dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
+    hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX>), dim3(blocks),
+                       dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, 0u);
     return hipGetLastError();
 }
 
@@ -1054,14 +1075,13 @@ uint32_t stream_rows(uint32_t cols) {
 // Streaming pays for rows of two steps (a Q4_0 row of 4096 weights, say)
 // once the tiles outnumber the resident waves (4096) by a margin; with one
 // step per row the one-shot kernel's many small workgroups read faster.
-// QMV_STREAM_MIN overrides the threshold.
 template <uint32_t WT>
 bool use_stream(const MatView* ms, uint32_t n) {
     const uint32_t nr = stream_rows<WT>(ms[0].cols);
     if (nr != 2) return false;
     uint64_t tiles = 0;
     for (uint32_t i = 0; i < n; ++i) tiles += (ms[i].rows + nr - 1) / nr;
-    return tiles >= QMV_KNOB("QMV_STREAM_MIN", 6144);
+    return tiles >= 6144;
 }
 
 // One streaming launch for a single activation vector (the decode case).
@@ -1098,7 +1118,6 @@ hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) 
     // sixteen-wave groups (one or two groups per compute unit)
     const bool wide = S >= 2 && S <= 4 && m.rows >= 16 * 256 && m.rows <= 2 * 16 * 256;
     if (wide) nr = 1;
-    nr = QMV_KNOB("QMV_GEMV_NR", nr);
     if (oneshot_fits<WT>(m.cols, NB, nr)) {
         const size_t l = static_cast<size_t>(gemv_lds_bytes<WT>(m.cols, NB));
 #define QMV_ONESHOT(NR_, SMAX_, W_) \
@@ -1171,7 +1190,7 @@ hipError_t gated_launch(const MatView& w1, const MatView& w3, uint32_t act, cons
     const uint32_t per_wg = (tiles + blocks - 1) / blocks;
     const size_t lds = static_cast<size_t>(gemv_lds_bytes<WT>(cols, NB));
     const float* xp = x + static_cast<uint64_t>(done) * cols;
-    hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, 2, true>), dim3(blocks),
+    hipLaunchKernelGGL((gemv_stream_kernel<WT, SF16, NR, NB, SMAX, true>), dim3(blocks),
                        dim3(kStreamWaves * 64), lds, s, g, xp, cols, per_wg, act);
     return hipGetLastError();
 }
@@ -1223,7 +1242,7 @@ hipError_t group_launch(const GroupArgs& g, uint32_t blocks, size_t lds, const f
 }
 
 // Rows per wave of a grouped launch: 1 (measured faster than 2 for a mixed
-// wq | wk | wv group); QMV_GROUP_NR = 2 selects two when cols <= 4096.
+// wq | wk | wv group); nr = 2 is built for cols <= 4096.
 template <int NB>
 hipError_t group_pass(const MatView* ms, uint32_t n, const float* x, float* const* ys,
                       uint32_t done, uint32_t nr, hipStream_t s) {
@@ -1262,7 +1281,7 @@ hipError_t group_pass(const MatView* ms, uint32_t n, const float* x, float* cons
 constexpr uint32_t kGemvMaxBatch = 8;
 
 hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, float* const* ys,
-                             uint32_t batch, hipStream_t s) {
+                             uint32_t batch, void* workspace, hipStream_t s) {
     const uint32_t cols = ms[0].cols;
     const uint32_t S4 = (cols / 32 + 63) / 64;
     const bool fits = n <= static_cast<uint32_t>(kMaxGroup) && batch <= kGemvMaxBatch && S4 <= 8 &&
@@ -1280,13 +1299,12 @@ hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, floa
     }
     if (!fits) {  // one launch per matrix
         for (uint32_t i = 0; i < n; ++i) {
-            const hipError_t e = launch_gemv(ms[i], x, ys[i], batch, s);
+            const hipError_t e = launch_gemv(ms[i], x, ys[i], batch, workspace, s);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
     }
-    const uint32_t nr_want = QMV_KNOB("QMV_GROUP_NR", 1);
-    const uint32_t nr = (S4 <= 2 && nr_want == 2) ? 2 : 1;  // the NR = 2 kernel has SMAX4 = 2
+    const uint32_t nr = 1;
     uint32_t done = 0;
     while (done < batch) {
         const uint32_t nb = pass_vectors<kQ4>(cols, batch - done);
@@ -1320,12 +1338,16 @@ hipError_t launch_gemv_gated(const MatView& w1, const MatView& w3, uint32_t act,
                         : gated_batched<kQ8, false>(w1, w3, act, x, h, batch, s);
 }
 
+size_t gemv_workspace_bytes(const MatView& m, uint32_t batch) {
+    if (batch <= kGemvMaxBatch || gemv_mfma_fits(m)) return 0;
+    return gemm_workspace_bytes(m, batch, true);
+}
+
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
-                       uint32_t batch, hipStream_t s) {
+                       uint32_t batch, void* workspace, hipStream_t s) {
     if (batch > kGemvMaxBatch) {
-        const hipError_t e = launch_gemv_mfma(m, x, y, batch, s);
-        if (e != hipErrorNotSupported) return e;
-        return launch_gemm(m, x, true, y, batch, nullptr, s);
+        if (gemv_mfma_fits(m)) return launch_gemv_mfma(m, x, y, batch, s);
+        return launch_gemm(m, x, true, y, batch, workspace, s);
     }
     if (m.wtype == kQ4) {
         return m.scale_f16 ? gemv_batched<kQ4, true>(m, x, y, batch, s)

@@ -303,15 +303,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
 
 }  // namespace
 
-hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
-                            hipStream_t s) {
+bool gemv_mfma_fits(const MatView& m) {
     // Q8_0 with f16 scales, cols 512 or 1024 (an even number of groups of 8
     // blocks, activations of one pass in LDS), and weights and outputs within
     // 32-bit buffer offsets
-    if (m.wtype != kQ8 || !m.scale_f16 || (m.cols != 512 && m.cols != 1024) ||
-        static_cast<uint64_t>(m.rows) * m.cols >= 0xFFFFFFF0ull ||
-        static_cast<uint64_t>(m.rows) * kTokens * 4 >= 0xFFFFFFF0ull)
-        return hipErrorNotSupported;
+    return m.wtype == kQ8 && m.scale_f16 && (m.cols == 512 || m.cols == 1024) &&
+           static_cast<uint64_t>(m.rows) * m.cols < 0xFFFFFFF0ull &&
+           static_cast<uint64_t>(m.rows) * kTokens * 4 < 0xFFFFFFF0ull;
+}
+
+hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
+                            hipStream_t s) {
+    if (!gemv_mfma_fits(m)) return hipErrorNotSupported;
     const float wscale = ldexpf(1.0f, 8 - m.dexp);
     const float inv = ldexpf(1.0f, m.dexp - 8);
     const uint32_t tiles = (m.rows + 31) / 32;

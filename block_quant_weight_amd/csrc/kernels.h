@@ -10,18 +10,25 @@ namespace qmv {
 struct MatView {
     const uint8_t* q;
     const void* d;
+    const int32_t* rexp;  // per row: largest finite |d| of the row in [2^(e-1), 2^e); 0 if none
     uint32_t wtype, scale_f16, rows, cols;
-    int32_t dexp;  // max |d| in [2^(dexp-1), 2^dexp); 0 if all zero or non-finite
+    int32_t dexp;         // the same over the whole matrix
 };
 
 // y[t][r] = sum_c W[r][c] x[t][c]; x f32 [batch][cols], y f32 [batch][rows].
+// Batches above 8 that the f16 LM-head kernel does not take run on the
+// GEMM, which stages the activations in `workspace` (gemv_workspace_bytes
+// of them; none needed when that is 0).
+size_t gemv_workspace_bytes(const MatView& m, uint32_t batch);
 hipError_t launch_gemv(const MatView& m, const float* x, float* y,
-                       uint32_t batch, hipStream_t stream);
+                       uint32_t batch, void* workspace, hipStream_t stream);
 
 // One launch for n <= 8 matrices with the same cols multiplying the same x:
 // ys[i] = W_i x (falls back to one launch per matrix when they do not fit).
+// (batches above 8 run matrix by matrix, with a workspace of the largest
+// gemv_workspace_bytes of the matrices).
 hipError_t launch_gemv_group(const MatView* ms, uint32_t n, const float* x, float* const* ys,
-                             uint32_t batch, hipStream_t stream);
+                             uint32_t batch, void* workspace, hipStream_t stream);
 
 // Gated pair of a feed-forward layer: h[t][r] = act(sum_c W1[r][c] x[t][c]) *
 // sum_c W3[r][c] x[t][c], act 0 = SiLU, 1 = GELU (tanh form), in one launch
@@ -33,13 +40,13 @@ bool gemv_gated_fits(const MatView& w1, const MatView& w3);
 hipError_t launch_gemv_gated(const MatView& w1, const MatView& w3, uint32_t act, const float* x,
                              float* h, uint32_t batch, hipStream_t stream);
 
-// Same product on the matrix cores: x is bf16 bits, or f32 split into two
-// bf16 terms (x_f32 = true).  Large batches may split K; the slices' partial
-// sums then go to `workspace` (gemm_workspace_bytes of them; ignored when
-// that is 0).
+// Same product on the matrix cores with f16 operands: x is bf16 bits, or
+// f32 (x_f32 = true).  The activations are first staged as scaled f16 in
+// `workspace`, which also holds the partial sums when K is split
+// (gemm_workspace_bytes of it, 256-byte aligned).
 size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
-                       uint32_t batch, float* workspace, hipStream_t stream);
+                       uint32_t batch, void* workspace, hipStream_t stream);
 
 // y[i] = sum over z < splits of part[z * total + i], added in z order.
 hipError_t launch_splitk_sum(const float* part, float* y, uint64_t total, uint32_t splits,
@@ -57,7 +64,8 @@ hipError_t launch_gemm_q8act(const MatView& m, const int8_t* xq, const float* dx
 
 // Batched product on the matrix cores with f16 operands (Q8_0 with f16
 // scales, cols 512 or 1024, any batch): returns hipErrorNotSupported for
-// other matrices, which then take launch_gemm.
+// other matrices (gemv_mfma_fits false), which then take launch_gemm.
+bool gemv_mfma_fits(const MatView& m);
 hipError_t launch_gemv_mfma(const MatView& m, const float* x, float* y, uint32_t batch,
                             hipStream_t stream);
 

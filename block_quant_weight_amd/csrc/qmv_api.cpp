@@ -14,9 +14,13 @@
 
 struct qmv_mat {
     qmv::Layout layout;
-    uint8_t* dev = nullptr;  // q at dev, d at dev + d_offset (hipMalloc'd)
+    // One hipMalloc: q at dev, d at dev + d_offset (the file image, d's
+    // padding zeroed), then at rexp_offset one int32 per row: the exponent
+    // of the row's largest finite scale magnitude.
+    uint8_t* dev = nullptr;
+    uint64_t rexp_offset = 0;
     int device = -1;
-    int32_t dexp = 0;        // exponent of the largest scale magnitude
+    int32_t dexp = 0;        // the same exponent over the whole matrix
 };
 
 namespace {
@@ -88,8 +92,31 @@ int workspace_for(hipStream_t stream, size_t bytes, void** out) {
 
 qmv::MatView view(const qmv_mat* h) {
     const qmv::Layout& L = h->layout;
-    return qmv::MatView{h->dev, h->dev + L.d_offset, L.wtype, L.scale_f16,
-                        L.rows, L.cols, h->dexp};
+    return qmv::MatView{h->dev, h->dev + L.d_offset,
+                        reinterpret_cast<const int32_t*>(h->dev + h->rexp_offset), L.wtype,
+                        L.scale_f16, L.rows, L.cols, h->dexp};
+}
+
+// Bytes of a handle's device allocation: the image with d's padding, then
+// the row exponents from a 64-byte boundary.
+bool device_bytes(const qmv::Layout& L, uint64_t* rexp_off, uint64_t* total) {
+    const uint64_t off = (L.full_span + 63) & ~uint64_t{63};
+    if (off < L.full_span) return false;
+    const uint64_t t = off + uint64_t{L.rows} * 4;
+    if (t < off) return false;
+    *rexp_off = off;
+    *total = t;
+    return true;
+}
+
+// The row exponents of a checked host buffer (image or GGUF blocks), copied
+// behind the image on `s`; the host vector must live until the stream is
+// synchronised.
+hipError_t upload_row_exponents(const qmv::Layout& L, const void* src, bool gguf, uint8_t* dst,
+                                std::vector<int32_t>& rexp, int32_t* dexp, hipStream_t s) {
+    rexp.resize(L.rows);
+    qmv::scale_exponents(L, src, gguf, rexp.data(), dexp);
+    return hipMemcpyAsync(dst, rexp.data(), uint64_t{L.rows} * 4, hipMemcpyHostToDevice, s);
 }
 
 }  // namespace
@@ -118,24 +145,30 @@ int qmv_upload(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
     if (st != QMV_OK) return st;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_DEVICE;
+    uint64_t rexp_off = 0, total = 0;
+    if (!device_bytes(L, &rexp_off, &total)) return QMV_E_SHAPE;
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, L.full_span);
+    hipError_t e = hipMalloc(&p, total);
     if (e != hipSuccess) return device_status(e);
     uint8_t* d = static_cast<uint8_t*>(p);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int32_t> rexp;
+    int32_t dexp = 0;
     e = hipMemcpyAsync(d, src, L.min_span, hipMemcpyHostToDevice, s);
     // The device image always carries d's zero padding, whether or not the
     // caller's buffer held it.
-    if (e == hipSuccess && L.full_span > L.min_span)
-        e = hipMemsetAsync(d + L.min_span, 0, L.full_span - L.min_span, s);
+    if (e == hipSuccess && rexp_off > L.min_span)
+        e = hipMemsetAsync(d + L.min_span, 0, rexp_off - L.min_span, s);
+    if (e == hipSuccess) e = upload_row_exponents(L, src, false, d + rexp_off, rexp, &dexp, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
         (void)hipFree(d);
         return device_status(e);
     }
     h->dev = d;
+    h->rexp_offset = rexp_off;
     h->device = dev;
-    h->dexp = qmv::scale_exponent(L, src);
+    h->dexp = dexp;
     return QMV_OK;
 }
 
@@ -151,9 +184,11 @@ int qmv_upload_gguf(qmv_handle h, const void* src, uint64_t nbytes, void* stream
     if (st != QMV_OK) return st;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return QMV_E_DEVICE;
+    uint64_t rexp_off = 0, total = 0;
+    if (!device_bytes(L, &rexp_off, &total)) return QMV_E_SHAPE;
     void* img = nullptr;
     void* raw = nullptr;
-    hipError_t e = hipMalloc(&img, L.full_span);
+    hipError_t e = hipMalloc(&img, total);
     if (e != hipSuccess) return device_status(e);
     e = hipMalloc(&raw, gb);
     if (e != hipSuccess) {
@@ -164,11 +199,14 @@ int qmv_upload_gguf(qmv_handle h, const void* src, uint64_t nbytes, void* stream
     uint8_t* d = static_cast<uint8_t*>(img);
     // the raw blocks to the device, the image zeroed (its padding), then
     // each block's quants and scale moved to the two arrays
+    std::vector<int32_t> rexp;
+    int32_t dexp = 0;
     e = hipMemcpyAsync(raw, src, gb, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipMemsetAsync(img, 0, L.full_span, s);
+    if (e == hipSuccess) e = hipMemsetAsync(img, 0, rexp_off, s);
     if (e == hipSuccess)
         e = qmv::launch_gguf_repack(L.wtype, raw, uint64_t{L.rows} * (L.cols / 32), d,
                                     reinterpret_cast<uint16_t*>(d + L.d_offset), s);
+    if (e == hipSuccess) e = upload_row_exponents(L, src, true, d + rexp_off, rexp, &dexp, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     (void)hipFree(raw);
     if (e != hipSuccess) {
@@ -176,8 +214,9 @@ int qmv_upload_gguf(qmv_handle h, const void* src, uint64_t nbytes, void* stream
         return device_status(e);
     }
     h->dev = d;
+    h->rexp_offset = rexp_off;
     h->device = dev;
-    h->dexp = qmv::scale_exponent_gguf(L, src);
+    h->dexp = dexp;
     return QMV_OK;
 }
 
@@ -200,8 +239,12 @@ int qmv_gemv(qmv_handle h, const float* x, float* y, uint32_t batch,
     if (st != QMV_OK) return st;
     if (x == nullptr || y == nullptr || batch == 0) return QMV_E_ARG;
     if (!aligned16(x) || !aligned16(y)) return QMV_E_ARG;
-    return device_status(qmv::launch_gemv(view(h), x, y, batch,
-                                          static_cast<hipStream_t>(stream)));
+    const qmv::MatView v = view(h);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    st = workspace_for(s, qmv::gemv_workspace_bytes(v, batch), &ws);
+    if (st != QMV_OK) return st;
+    return device_status(qmv::launch_gemv(v, x, y, batch, ws, s));
 }
 
 int qmv_gemv_group(const qmv_handle* hs, uint32_t n, const float* x, float* const* ys,
@@ -210,15 +253,21 @@ int qmv_gemv_group(const qmv_handle* hs, uint32_t n, const float* x, float* cons
         return QMV_E_ARG;
     if (!aligned16(x)) return QMV_E_ARG;
     qmv::MatView ms[8];
+    size_t wsb = 0;
     for (uint32_t i = 0; i < n; ++i) {
         const int st = ready(hs[i]);
         if (st != QMV_OK) return st;
         if (ys[i] == nullptr || !aligned16(ys[i])) return QMV_E_ARG;
         ms[i] = view(hs[i]);
         if (ms[i].cols != ms[0].cols) return QMV_E_SHAPE;
+        const size_t b = qmv::gemv_workspace_bytes(ms[i], batch);
+        wsb = b > wsb ? b : wsb;
     }
-    return device_status(qmv::launch_gemv_group(ms, n, x, ys, batch,
-                                                static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    const int st = workspace_for(s, wsb, &ws);
+    if (st != QMV_OK) return st;
+    return device_status(qmv::launch_gemv_group(ms, n, x, ys, batch, ws, s));
 }
 
 int qmv_gemv_gated(qmv_handle w1, qmv_handle w3, uint32_t act, const float* x, float* h,
@@ -248,8 +297,7 @@ int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
     void* ws = nullptr;
     st = workspace_for(s, qmv::gemm_workspace_bytes(v, batch, false), &ws);
     if (st != QMV_OK) return st;
-    return device_status(qmv::launch_gemm(v, x_bf16, false, y, batch,
-                                          static_cast<float*>(ws), s));
+    return device_status(qmv::launch_gemm(v, x_bf16, false, y, batch, ws, s));
 }
 
 int qmv_gemm_q8(qmv_handle h, const int8_t* xq, const float* dx, float* y, uint32_t batch,

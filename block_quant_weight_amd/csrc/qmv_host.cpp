@@ -113,65 +113,84 @@ int check_gguf(const Layout& L, const void* src, uint64_t nbytes) {
 }
 
 namespace {
-// exponent of the largest of the f16 magnitudes (low 15 bits) m
-int32_t f16_max_exponent(uint16_t m) {
-    if (m >= 0x7C00) return 0;  // inf or NaN
-    const int e = m >> 10, f = m & 0x3FF;
-    const float amax = e == 0 ? std::ldexp(static_cast<float>(f), -24)
-                              : std::ldexp(static_cast<float>(1024 + f), e - 25);
-    if (amax == 0.f) return 0;
-    int ex = 0;
-    (void)std::frexp(amax, &ex);
-    return ex;
+// Binary exponent E of a finite magnitude a > 0 (a in [2^(E-1), 2^E)).
+int32_t exponent_of(float a) {
+    int e = 0;
+    (void)std::frexp(a, &e);
+    return e;
 }
+
+// Largest finite magnitude among scales held as f16 bits (low 15 bits
+// compared as integers: binary16 magnitudes order like their bit patterns),
+// or 0 when there is none.
+struct F16Max {
+    uint16_t m = 0;
+    void add(uint16_t b) {
+        b &= 0x7FFF;
+        if (b < 0x7C00 && b > m) m = b;  // inf and NaN patterns are skipped
+    }
+    int32_t exponent() const {
+        if (m == 0) return 0;
+        const int e = m >> 10, f = m & 0x3FF;
+        const float a = e == 0 ? std::ldexp(static_cast<float>(f), -24)
+                               : std::ldexp(static_cast<float>(1024 + f), e - 25);
+        return exponent_of(a);
+    }
+};
+
+// The same for float32 scales (magnitudes order like their low 31 bits).
+struct F32Max {
+    uint32_t m = 0;
+    void add(uint32_t b) {
+        b &= 0x7FFFFFFFu;
+        if (b < 0x7F800000u && b > m) m = b;
+    }
+    int32_t exponent() const {
+        if (m == 0) return 0;
+        float a;
+        __builtin_memcpy(&a, &m, 4);
+        return exponent_of(a);
+    }
+};
 }  // namespace
 
-int32_t scale_exponent_gguf(const Layout& L, const void* src) {
+void scale_exponents(const Layout& L, const void* src, bool gguf, int32_t* row_exp,
+                     int32_t* mat_exp) {
     const uint8_t* p = static_cast<const uint8_t*>(src);
-    const uint64_t blocks = uint64_t{L.rows} * (L.cols / 32);
-    const uint64_t bsize = L.wtype == QMV_Q8_0 ? 34 : 18;
-    uint16_t m = 0;
-    for (uint64_t k = 0; k < blocks; ++k) {
-        uint16_t b;
-        __builtin_memcpy(&b, p + k * bsize, 2);
-        b &= 0x7FFF;
-        m = b > m ? b : m;
-    }
-    return f16_max_exponent(m);
-}
-
-int32_t scale_exponent(const Layout& L, const void* src) {
-    const uint8_t* d = static_cast<const uint8_t*>(src) + L.d_offset;
-    const uint64_t n = L.d_bytes / (L.scale_f16 ? 2 : 4);
-    float amax = 0.f;
-    if (L.scale_f16) {
-        // magnitudes of IEEE binary16 values order like their low 15 bits
-        uint16_t m = 0;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint16_t b;
-            __builtin_memcpy(&b, d + 2 * i, 2);
-            b &= 0x7FFF;
-            m = b > m ? b : m;
+    const uint64_t nblk = L.cols / 32;
+    if (gguf || L.scale_f16) {
+        // GGUF: the f16 scale opens each 18- or 34-byte block; .mlb: the d array
+        const uint64_t stride = gguf ? (L.wtype == QMV_Q8_0 ? 34 : 18) : 2;
+        const uint8_t* d = gguf ? p : p + L.d_offset;
+        F16Max all;
+        for (uint64_t r = 0; r < L.rows; ++r) {
+            F16Max row;
+            const uint8_t* dr = d + r * nblk * stride;
+            for (uint64_t b = 0; b < nblk; ++b) {
+                uint16_t v;
+                __builtin_memcpy(&v, dr + b * stride, 2);
+                row.add(v);
+            }
+            all.add(row.m);
+            if (row_exp) row_exp[r] = row.exponent();
         }
-        if (m >= 0x7C00) return 0;  // inf or NaN
-        const int e = m >> 10, f = m & 0x3FF;
-        amax = e == 0 ? std::ldexp(static_cast<float>(f), -24)
-                      : std::ldexp(static_cast<float>(1024 + f), e - 25);
-    } else {
-        uint32_t m = 0;
-        for (uint64_t i = 0; i < n; ++i) {
-            uint32_t b;
-            __builtin_memcpy(&b, d + 4 * i, 4);
-            b &= 0x7FFFFFFFu;
-            m = b > m ? b : m;
-        }
-        if (m >= 0x7F800000u) return 0;
-        __builtin_memcpy(&amax, &m, 4);
+        *mat_exp = all.exponent();
+        return;
     }
-    if (amax == 0.f) return 0;
-    int e = 0;
-    (void)std::frexp(amax, &e);
-    return e;
+    const uint8_t* d = p + L.d_offset;
+    F32Max all;
+    for (uint64_t r = 0; r < L.rows; ++r) {
+        F32Max row;
+        const uint8_t* dr = d + r * nblk * 4;
+        for (uint64_t b = 0; b < nblk; ++b) {
+            uint32_t v;
+            __builtin_memcpy(&v, dr + b * 4, 4);
+            row.add(v);
+        }
+        all.add(row.m);
+        if (row_exp) row_exp[r] = row.exponent();
+    }
+    *mat_exp = all.exponent();
 }
 
 }  // namespace qmv

@@ -29,13 +29,15 @@ int gguf_bytes(uint32_t wtype, uint32_t rows, uint32_t cols, uint64_t* bytes);
 // no Q8_0 quant equal to -128.  QMV_OK, QMV_E_ARG or QMV_E_FORMAT.
 int check_gguf(const Layout& L, const void* src, uint64_t nbytes);
 
-// scale_exponent for GGUF block data (the scale of block k at k * 18 / 34).
-int32_t scale_exponent_gguf(const Layout& L, const void* src);
-
-// Binary exponent E of the largest scale magnitude of a checked buffer
-// (max |d| in [2^(E-1), 2^E)); 0 when every scale is zero or some scale is
-// inf or NaN.  Kernels that hold weights in a narrow float type scale them
-// by 2^-E so that no product overflows.
-int32_t scale_exponent(const Layout& L, const void* src);
+// Binary exponent E (largest magnitude in [2^(E-1), 2^E)) of the largest
+// finite scale magnitude of each row (row_exp[r], if row_exp is not null)
+// and of the whole matrix (*mat_exp) of a checked buffer: the two-array
+// image (gguf false) or GGUF block data (gguf true, the f16 scale at the
+// start of each block).  0 where every finite scale is zero.  Non-finite
+// scales are skipped: their products are non-finite however the weights
+// are scaled.  Kernels that hold weights in f16 scale a row by 2^(8 - E),
+// so that its largest weight stays below 2^15.
+void scale_exponents(const Layout& L, const void* src, bool gguf, int32_t* row_exp,
+                     int32_t* mat_exp);
 
 }  // namespace qmv

@@ -27,11 +27,13 @@
  *
  * Streams: `stream` is a hipStream_t passed as a pointer; NULL is the null
  * stream.  Compute calls only enqueue work on it and return; they never
- * synchronize.  The one exception to "no allocation": a qmv_gemm or
- * qmv_gemm_q8 call that splits K keeps its partial sums in a workspace owned by the
- * library, one per (device, stream), allocated on first need and grown (never
- * freed) for a larger batch; that first call on a stream must not be made
- * while the stream is being captured into a graph (QMV_E_ARG).
+ * synchronize.  The one exception to "no allocation": the matrix-core
+ * products (qmv_gemm, qmv_gemm_q8 when it splits K, and qmv_gemv on batches
+ * above 8 that the f16 LM-head kernel does not take) keep staged
+ * activations and partial sums in a workspace owned by the library, one per
+ * (device, stream), allocated on first need and grown (never freed) for a
+ * larger call; such a first call on a stream must not be made while the
+ * stream is being captured into a graph (QMV_E_ARG).
  *
  * Pointers: `x`, `y`, `ids`, `out`, `q`, `d`, `s` of the compute calls are
  * device pointers owned by the caller, each 16-byte aligned (QMV_E_ARG
@@ -151,31 +153,32 @@ int qmv_destroy(qmv_handle h);
  * Decode product (GEMV), y[t][r] = sum_c W[r][c] * x[t][c], for t < batch.
  * x: float32 [batch][cols], y: float32 [batch][rows], row-major, device
  * memory.  The weights stay quantized in device memory and are decoded in
- * registers.
+ * registers.  Every output is within 2e-3 * sum_c |W[r][c]| |x[t][c]| of
+ * the exact product (the .mlb page's "Body" defines the product; the bound
+ * is the parity bar), by these means:
  * Batches up to 8 run the bandwidth-bound vector kernels: every activation is
  * represented, per block of 32 (the span of one weight scale), in 24-bit
- * fixed point relative to the block's largest magnitude amax (an error of at
- * most 2^-22 * amax), the block sums of weight codes times activation digits
- * are exact integer dot products (the Q8_0 activation quantization of the
- * .mlb page's "Quantization rule", with three int8 digits instead of one),
- * and blocks are accumulated in float32.  An output is then within
- * 2^-22 * sum_b amax_b * sum_{c in b} |W[r][c]| of the exact product, plus
- * float32 rounding; this is within 2e-3 * sum_c |W[r][c]| |x[t][c]| unless,
- * inside blocks, the nonzero weights meet only activations below about
- * amax / 8000.  A non-finite activation makes the outputs of its batch row
- * NaN.  Larger batches (an LM head over a batch of hidden states, say) run
- * on the matrix cores: for a Q8_0 matrix with f16 scales and cols a multiple
- * of 256 up to 1024, in f16 — each token's activations scaled by a power of
- * two and rounded to f16, each weight fl16(q * d * 2^k) with one k for the
- * matrix (from its largest scale, found at upload) — with float32
- * accumulation, within about 2^-10 * sum_c |W[r][c]| |x[t][c]| for
- * activations within 2^28 of their token's largest and scales within 2^22
- * of the matrix's largest; otherwise with weights rounded to bfloat16 and
- * each float32 activation split into two bfloat16 terms, within
- * 2e-3 * sum_c |W[r][c]| |x[t][c]|.  A non-finite activation makes its
- * token's outputs NaN on the f16 path.
- * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no upload),
- * QMV_E_DEVICE (launch failure).
+ * fixed point relative to the block's largest magnitude amax, the block sums
+ * of weight codes times activation digits are exact integer dot products
+ * (the Q8_0 activation quantization of the .mlb page's "Quantization rule",
+ * with three int8 digits instead of one), and blocks are accumulated in
+ * float32.  A block holding a nonzero activation more than 2^12 below its
+ * amax (which the fixed point would keep to worse than 2^-11 of itself) is
+ * multiplied in float32 from the activations instead.  A non-finite
+ * activation makes the outputs of its batch row NaN.
+ * Larger batches (an LM head over a batch of hidden states, say) run on the
+ * matrix cores with f16 operands and float32 accumulation: each token's
+ * activations scaled by a power of two from its largest magnitude and
+ * rounded to f16; each weight fl16(q * d * 2^k), k one per matrix (the f16
+ * LM-head kernel: Q8_0 with f16 scales and 512 or 1024 columns) or one per
+ * row (every other matrix), from the largest finite scale, found at upload.
+ * This is within about 2^-10 * sum_c |W[r][c]| |x[t][c]| for activations
+ * within 2^28 of their token's largest and scales within 2^20 of the
+ * largest of their row (matrix, for the LM-head kernel); a non-finite
+ * activation makes its token's outputs NaN.
+ * Errors: QMV_E_ARG (null or misaligned pointer, batch 0, no upload, a first
+ * matrix-core call on a stream under graph capture), QMV_E_NOMEM
+ * (workspace), QMV_E_DEVICE (launch failure).
  */
 int qmv_gemv(qmv_handle h, const float *x, float *y, uint32_t batch,
              void *stream);
@@ -219,13 +222,20 @@ int qmv_gemv_gated(qmv_handle w1, qmv_handle w3, uint32_t act, const float *x,
 /*
  * Prefill product (GEMM), y[t][r] = sum_c W[r][c] * x[t][c], with x given
  * as bfloat16 bit patterns: x_bf16 uint16 [batch][cols], y float32
- * [batch][rows], device memory.  Tiles of W are decoded to bfloat16
- * (w rounded to nearest even) in LDS and multiplied on the matrix cores with
- * float32 accumulation.  When the matrix has too few tiles to fill the GPU
- * the K dimension is split and the slices' partial sums are added in slice
- * order by a second kernel (deterministic).  Errors: as qmv_gemv, plus
- * QMV_E_ARG for a first split-K call on a stream under graph capture and
- * QMV_E_NOMEM if its workspace cannot be allocated.
+ * [batch][rows], device memory.  On the matrix cores with f16 operands and
+ * float32 accumulation: a first kernel stages each token's activations in
+ * f16, scaled by a power of two from the token's largest magnitude (exact for
+ * values within 2^31 of it); each weight enters as fl16(v * d * 2^(8 - E_r)),
+ * E_r the exponent of row r's largest finite scale (found at upload), so a
+ * weight keeps 2^-11 relative precision when its scale is within 2^20 of
+ * the row's largest; the outputs are scaled back exactly.  Every output is
+ * within 2e-3 * sum_c |W[r][c]| |x[t][c]| of the exact product over that
+ * range (2^-11 for the weights plus the float32 accumulation); a token
+ * holding inf or NaN gets NaN outputs.  When the matrix has too few tiles to
+ * fill the GPU the K dimension is split and the slices' partial sums are
+ * added in slice order by a third kernel (deterministic).  Errors: as
+ * qmv_gemv, plus QMV_E_ARG for a first call on a stream under graph capture
+ * and QMV_E_NOMEM if its workspace cannot be allocated.
  */
 int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
              void *stream);

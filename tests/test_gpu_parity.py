@@ -387,35 +387,6 @@ def test_gemv_group_rejects_mismatched_cols():
         Q.qmv_destroy(b)
 
 
-@pytest.mark.parametrize("wt,sf", [(K.Q8, 0), (K.Q4, 1)])
-def test_gemv_activation_representation_bound(wt, sf):
-    # Activations spanning 2^40 inside each block of 32.  The vector kernels
-    # keep every activation to 2^-22 of its block's largest magnitude, so an
-    # output is within 2^-22 * sum_b amax_b * sum_{c in b} |w| of the exact
-    # product (plus float32 rounding): the bound the header states, which
-    # the 2e-3 * sum |w||x| tolerance alone does not cover for such blocks.
-    R, C, B = 96, 256, 3
-    img = K.make_image(91, 0, wt, sf, R, C)
-    h = K.upload(img, wt, sf, R, C)
-    try:
-        g = np.random.default_rng(91)
-        mag = np.exp2(-g.uniform(0.0, 40.0, size=(B, C)))
-        x = (g.choice([-1.0, 1.0], size=(B, C)) * mag).astype(np.float32)
-        x[:, 5] = np.float32(2.0 ** 20)          # one dominant value per vector
-        ref, norm = O.product(img, wt, sf, R, C, x)
-        w = O.dequant_rows(img, wt, sf, R, C, np.arange(R, dtype=np.int64)).astype(np.float64)
-        amax = np.abs(x.astype(np.float64)).reshape(B, C // 32, 32).max(axis=2)
-        wabs = np.abs(w).reshape(R, C // 32, 32).sum(axis=2)
-        bound = 2.0 ** -22 * (amax @ wabs.T) + 2e-6 * norm
-        y = K.gpu_gemv(h, x).astype(np.float64)
-        err = np.abs(y - ref)
-        worst = float(np.max(err / np.maximum(bound, 1e-300)))
-        print(f"worst |y-ref| / bound = {worst:.3e}")
-        assert np.all(err <= bound), f"outside the stated bound (worst ratio {worst:.3e})"
-    finally:
-        Q.qmv_destroy(h)
-
-
 def test_gemv_nonfinite_activation_gives_nan():
     R, C = 64, 128
     img = K.make_image(92, 0, K.Q4, 1, R, C)
