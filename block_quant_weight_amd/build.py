@@ -40,7 +40,19 @@ def _run(cmd):
     return p
 
 
-def build(verbose: bool = False) -> str:
+def _stale(obj: str, src: str) -> bool:
+    """True when obj is missing or older than its source or any header."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps += [os.path.join(INCLUDE, h) for h in os.listdir(INCLUDE)]
+    return any(os.path.getmtime(dp) > t for dp in deps)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compiles every source (incremental=True: only those whose object is
+    older than the source or a header) and links libqmv.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
@@ -53,11 +65,12 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append((obj, ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE,
                            "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]))
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        for obj, cmd in jobs:
+    todo = [j for j in jobs if not incremental or _stale(j[0], j[1][-3])]
+    with ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
+        for obj, cmd in todo:
             if verbose:
                 print(" ".join(cmd), file=sys.stderr)
-        list(ex.map(lambda j: _run(j[1]), jobs))
+        list(ex.map(lambda j: _run(j[1]), todo))
     tmp = LIB_PATH + ".tmp"
     _run(["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
           *[o for o, _ in jobs]])
@@ -66,4 +79,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -4,7 +4,9 @@
 // "Body"; w = q * d for Q8_0, w = (nibble - 8) * d for Q4_0 with byte j of a
 // block holding element j low and j + 16 high, sections "Q8_0" and "Q4_0"),
 // t over the batch of activation rows.  This is the one place where the
-// product is a dense contraction, so it runs on v_mfma_f32_16x16x32_f16.
+// product is a dense contraction, so it runs on v_mfma_f32_32x32x16_f16
+// (measured at 1.76 PFLOP/s back to back on this GPU, against 1.2 for the
+// 16x16x32 form).
 //
 // Numbers.  Each operand is held in f16 with a power-of-two scale chosen so
 // that the f16 values neither overflow nor lose relative precision:
@@ -26,29 +28,33 @@
 // within about 2^-10 * sum_c |W[r][c]| |X[t][c]|.
 //
 // Staging.  A first kernel writes the scaled f16 activations in the order
-// in which the matrix cores read their A operand: for a tile of 16 tokens
-// and a block of 32 columns, one contiguous 1 KiB fragment whose 16-byte
-// piece l = 16 g + m holds token m's columns 8 g .. 8 g + 7.  A wave then
-// loads each A operand with one fully coalesced 1 KiB load, and the
-// activations never pass through LDS.
+// in which the matrix cores read their A operand: for a tile of 32 tokens
+// and a block of 32 columns, two contiguous 1 KiB fragments (k slices s = 0,
+// 1) whose 16-byte piece 32 h + m holds token m's columns 8 g .. 8 g + 7 of
+// the block, g = 2 s + h.  A wave then loads each A operand with one fully
+// coalesced 1 KiB load, and the activations never pass through LDS.
 //
-// Product kernel.  A workgroup of 8 waves owns BM = 64 * WMW tokens x BN =
-// 16 * NT matrix rows and walks its slice of K in steps of KG = 8 / WMW
-// blocks of 32 columns.  Wave (wm, kg) multiplies tokens [64 wm, 64 wm + 64)
-// of the tile by the NT row tiles over block kg of every step (4 x NT
-// 16x16x32 products per step), the KG groups' sums meeting in LDS at the end.
-// Per step, the workgroup decodes the tile's weights once into LDS, in the
-// B-operand order (1 KiB per 16 rows x 32 columns, lane piece 16 g + n =
-// row n's columns 8 g .. 8 g + 7), double-buffered; each thread decodes
-// half blocks: a Q4_0 half block (bytes 8 h .. 8 h + 7) holds columns
-// 8 h .. 8 h + 7 in its low nibbles and 16 + 8 h .. in its high nibbles,
-// so its two pieces are g = h and g = 2 + h; a Q8_0 half block (bytes
-// 16 h .. 16 h + 15) gives g = 2 h and 2 h + 1.  Sixteen consecutive
-// threads take sixteen consecutive rows, so that their pieces fill 256
-// contiguous bytes of LDS (every bank once) and a wave's quant loads cover
-// 16 rows x 32 bytes.  Weight loads run DEPTH steps ahead in a ring of
-// register sets, activation loads one step ahead; all loads are raw buffer
-// loads, with an out-of-range offset (zeros, no traffic) past any edge.
+// Product kernel.  A workgroup of 8 waves owns 256 tokens x 128 matrix rows
+// and walks its slice of K in steps of two blocks of 32 columns.  Wave (wm,
+// kg) multiplies tokens [64 wm, 64 wm + 64) of the tile by the tile's four
+// 32-row tiles over block kg of every step (2 x 4 x 2 products per step).
+// Per step, the workgroup decodes the tile's weights once into LDS in the
+// B-operand order (fragments of 32 rows x 16 columns; lane 32 h + n of a
+// fragment = row n's columns 8 g .. 8 g + 7 of the block, g = 2 s + h),
+// double-buffered, with one barrier per step.  Each thread decodes one half
+// block per step: a Q4_0 half block (bytes 8 h .. 8 h + 7) holds element
+// groups g = h (low nibbles) and g = 2 + h (high); a Q8_0 half block (bytes
+// 16 h .. 16 h + 15) holds g = 2 h and 2 h + 1.  Four consecutive threads
+// take one row's two blocks of a step, so that a wave's quant load covers
+// 16 rows x 32 (or 64) contiguous bytes, the pattern the address units
+// serve fastest.  Each step first requests its activations two steps ahead
+// and then its weights three steps ahead (loads complete in order, so the
+// activations never wait behind a weight load of the same step); all loads
+// are raw buffer loads, with an out-of-range offset (zeros, no traffic)
+// past any edge.  At the end the two k groups exchange half of their sums
+// through LDS, and each wave scales and stores two of the four row tiles
+// (token shifts from LDS, raw buffer stores that drop what lies past the
+// last token or row).
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin by launch
 // index; the launch index is mapped so that each XCD gets a contiguous run
@@ -74,11 +80,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Activation staging: one workgroup per token (and one per padding token up
-// to a multiple of 16, which writes zeros).
+// Activation staging: one workgroup of 256 threads per token (and one per
+// padding token up to a multiple of 32, which writes zeros).  Each thread
+// holds up to 8 pieces of 8 values; all of them are requested before any is
+// used, so a token costs one round trip to memory (rows of more than 16384
+// values are taken in chunks, read twice).
 // ---------------------------------------------------------------------------
 
-constexpr int kTokenTop = 14;  // a token's largest staged magnitude is in [2^13, 2^14)
+constexpr int kTokenTop = 14;    // a token's largest staged magnitude is in [2^13, 2^14)
+constexpr int kStagePieces = 8;  // pieces per thread per chunk
+constexpr int kTokensPerTile = 32;
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
@@ -92,23 +103,51 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(a, b);
 }
 
-// The 8 values of piece p (columns 8p .. 8p + 7) of token row xr as float32.
+// Raw data of one piece (8 values): bf16 bits in r[0..3], or f32 in r[0..7].
 template <bool XF32>
-__device__ __forceinline__ void load_piece(const void* __restrict__ xr, uint32_t p, float (&v)[8]) {
+struct Piece {
+    uint32_t r[XF32 ? 8 : 4];
+};
+
+template <bool XF32>
+__device__ __forceinline__ Piece<XF32> load_piece(const uint8_t* __restrict__ xr, uint32_t p, bool ok) {
+    Piece<XF32> v;
     if constexpr (XF32) {
-        const float4* s = reinterpret_cast<const float4*>(xr) + 2 * p;
-        const float4 a = s[0], b = s[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        const uint4 a = ok ? reinterpret_cast<const uint4*>(xr)[2 * p] : make_uint4(0, 0, 0, 0);
+        const uint4 b = ok ? reinterpret_cast<const uint4*>(xr)[2 * p + 1] : make_uint4(0, 0, 0, 0);
+        v.r[0] = a.x; v.r[1] = a.y; v.r[2] = a.z; v.r[3] = a.w;
+        v.r[4] = b.x; v.r[5] = b.y; v.r[6] = b.z; v.r[7] = b.w;
     } else {
-        const uint4 w = reinterpret_cast<const uint4*>(xr)[p];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __builtin_bit_cast(float, ws[i] << 16);
-            v[2 * i + 1] = __builtin_bit_cast(float, ws[i] & 0xFFFF0000u);
-        }
+        const uint4 a = ok ? reinterpret_cast<const uint4*>(xr)[p] : make_uint4(0, 0, 0, 0);
+        v.r[0] = a.x; v.r[1] = a.y; v.r[2] = a.z; v.r[3] = a.w;
     }
+    return v;
+}
+
+template <bool XF32>
+__device__ __forceinline__ float piece_value(const Piece<XF32>& v, int i) {
+    if constexpr (XF32) return __builtin_bit_cast(float, v.r[i]);
+    else return __builtin_bit_cast(float, (i & 1) ? (v.r[i >> 1] & 0xFFFF0000u) : (v.r[i >> 1] << 16));
+}
+
+template <bool XF32>
+__device__ __forceinline__ uint32_t piece_max(const Piece<XF32>& v) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, __builtin_bit_cast(uint32_t, piece_value<XF32>(v, i)) & 0x7FFFFFFFu);
+    return m;
+}
+
+template <bool XF32>
+__device__ __forceinline__ uint4 piece_f16(const Piece<XF32>& v, int sh, bool bad) {
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16x2 h = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(piece_value<XF32>(v, 2 * i), sh)),
+                         static_cast<_Float16>(__builtin_amdgcn_ldexpf(piece_value<XF32>(v, 2 * i + 1), sh))};
+        o[i] = bad ? 0x7E007E00u : __builtin_bit_cast(uint32_t, h);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 template <bool XF32>
@@ -116,13 +155,20 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const void* __restrict__ x
                                                       uint32_t K, uint4* __restrict__ xs,
                                                       int32_t* __restrict__ tshift) {
     __shared__ uint32_t red[4];
-    const uint32_t t = blockIdx.x;
+    // token of this workgroup: workgroups go to the 8 XCDs round-robin, so
+    // contiguous runs of tokens are given to one XCD (when the padded batch
+    // allows) and each 32-token fragment is assembled in one L2, not
+    // written in 16-byte parts from eight
+    const uint32_t nwg = gridDim.x, id = blockIdx.x;
+    const uint32_t t = (nwg % (8 * kTokensPerTile)) == 0 ? (id & 7) * (nwg >> 3) + (id >> 3) : id;
     const int tid = threadIdx.x;
     const uint32_t npiece = K / 8, KB = K / 32;
-    const uint32_t mt = t >> 4, m = t & 15;
-    // piece p goes to fragment (mt, p / 4), slot 16 (p % 4) + m
-    uint4* const dst = xs + static_cast<uint64_t>(mt) * KB * 64 + m;
-    auto slot = [&](uint32_t p) { return (p >> 2) * 64 + (p & 3) * 16; };
+    const uint32_t mt = t / kTokensPerTile, m = t % kTokensPerTile;
+    // piece p (block p / 4, group g = p % 4: slice g / 2, half g % 2) goes to
+    // fragment (mt, p / 4, g / 2), slot 32 (g % 2) + m
+    uint4* const dst = xs + static_cast<uint64_t>(mt) * KB * 128 + m;
+    auto slot = [&](uint32_t p) { return (p >> 2) * 128 + ((p >> 1) & 1) * 64 + (p & 1) * 32; };
+    constexpr uint32_t CH = 256 * kStagePieces;  // pieces per chunk
     if (t >= M) {
         for (uint32_t p = tid; p < npiece; p += 256) dst[slot(p)] = make_uint4(0, 0, 0, 0);
         if (tid == 0) tshift[t] = 0;
@@ -131,12 +177,16 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const void* __restrict__ x
     const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<uint64_t>(t) * K * (XF32 ? 4 : 2);
     // largest magnitude as an integer maximum of the magnitude bits, so that
     // inf and NaN win over every finite value
+    Piece<XF32> v[kStagePieces];
     uint32_t mx = 0;
-    for (uint32_t p = tid; p < npiece; p += 256) {
-        float v[8];
-        load_piece<XF32>(xr, p, v);
+    for (uint32_t c0 = 0; c0 < npiece; c0 += CH) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mx = max(mx, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
+        for (int i = 0; i < kStagePieces; ++i) {
+            const uint32_t p = c0 + tid + 256 * i;
+            v[i] = load_piece<XF32>(xr, p, p < npiece);
+        }
+#pragma unroll
+        for (int i = 0; i < kStagePieces; ++i) mx = max(mx, piece_max<XF32>(v[i]));
     }
     mx = wave_max_u32(mx);
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -144,17 +194,20 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const void* __restrict__ x
     mx = max(max(red[0], red[1]), max(red[2], red[3]));
     const bool bad = mx >= 0x7F800000u;
     const int sh = (bad || mx == 0) ? 0 : kTokenTop - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mx));
-    for (uint32_t p = tid; p < npiece; p += 256) {
-        float v[8];
-        load_piece<XF32>(xr, p, v);
-        uint32_t o[4];
+    // the last chunk is still in registers; earlier ones are read again
+    const uint32_t last = npiece == 0 ? 0 : (npiece - 1) / CH * CH;
+    for (uint32_t c0 = 0; c0 < last; c0 += CH) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f16x2 h = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(v[2 * i], sh)),
-                       static_cast<_Float16>(__builtin_amdgcn_ldexpf(v[2 * i + 1], sh))};
-            o[i] = bad ? 0x7E007E00u : __builtin_bit_cast(uint32_t, h);
+        for (int i = 0; i < kStagePieces; ++i) {
+            const uint32_t p = c0 + tid + 256 * i;
+            const Piece<XF32> w = load_piece<XF32>(xr, p, p < npiece);
+            if (p < npiece) dst[slot(p)] = piece_f16<XF32>(w, sh, bad);
         }
-        dst[slot(p)] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < kStagePieces; ++i) {
+        const uint32_t p = last + tid + 256 * i;
+        if (p < npiece) dst[slot(p)] = piece_f16<XF32>(v[i], sh, bad);
     }
     if (tid == 0) tshift[t] = sh;
 }
@@ -168,32 +221,47 @@ namespace mm {
 constexpr int kThreads = 512;
 constexpr int kWeightTop = 8;  // a row's largest |scale| * 2^(8 - E_r) is below 2^8
 
-template <uint32_t WT, int NT, int WMW>
+// B fragments in LDS: 1 KiB of operand (lanes 0-31 then lanes 32-63, 512
+// bytes each, with 64 bytes between the halves), fragments 1280 bytes apart,
+// and the fragments of block b of a step shifted by b * 128 bytes.  A wave's
+// 16-byte fragment read stays 256 contiguous bytes per 16 lanes, and the
+// decode's writes (16 lanes: 4 rows x the 4 half blocks of a row) fall on
+// 16 different 16-byte bank groups.
+constexpr uint32_t kFragStride = 1280;
+constexpr uint32_t frag_off(uint32_t b, uint32_t f, uint32_t slot) {
+    return f * kFragStride + b * 128 + (slot >> 5) * 64 + slot * 16;
+}
+
+template <uint32_t WT, bool SF16>
 struct Cfg {
-    static constexpr int KG = 8 / WMW;                   // k groups = blocks per step
-    static constexpr int BM = 64 * WMW;                  // tokens per tile
-    static constexpr int BN = 16 * NT;                   // matrix rows per tile
-    static constexpr int UNITS = 2 * BN * KG;            // half blocks decoded per step
-    static constexpr int UPT = (UNITS + kThreads - 1) / kThreads;
-    static constexpr int QW = WT == kQ4 ? 2 : 4;         // quant words per half block
-    static constexpr int STAGE = KG * NT * 1024;         // bytes of one LDS stage
-    // the k groups' partial sums meet in LDS, JR row tiles at a time
-    static constexpr int RED_J = (KG - 1) * WMW * 4096;  // bytes per row tile
-    static constexpr int JR = (128 * 1024) / RED_J < NT ? (128 * 1024) / RED_J : NT;
-    // two stages, then 1 KiB that threads without a half block write their
-    // (zero) pieces to, so that the decode needs no branch
-    static constexpr int DUMMY = 2 * STAGE;
-    static constexpr int LDS = DUMMY + 1024 > JR * RED_J ? DUMMY + 1024 : JR * RED_J;
-    // steps of weight loads in flight: a ring of register sets, shorter when
-    // a thread decodes several half blocks per step
-    static constexpr int DEPTH = UPT == 1 ? 4 : 2;
+    static constexpr int NT = 4;                          // 32-row tiles per workgroup
+    static constexpr int KG = 2;                          // blocks per step = k groups of waves
+    static constexpr int WM = 4;                          // token waves of 64 per k group
+    static constexpr int BM = 64 * WM;                    // tokens per tile
+    static constexpr int BN = 32 * NT;                    // matrix rows per tile
+    static constexpr int QW = WT == kQ4 ? 2 : 4;          // quant words per half block
+    static constexpr uint32_t BLK_Q = WT == kQ4 ? 16 : 32;  // quant bytes per block
+    static constexpr uint32_t SB = SF16 ? 2 : 4;            // bytes per scale
+    static constexpr int STAGE = 2 * KG * NT * kFragStride + 256;  // one B stage
+    // at the end each wave hands half its row tiles to the wave of the other
+    // k group through LDS (the stages are free then), after the tile's token
+    // shifts
+    static constexpr int RED = KG * WM * (NT / 2) * 2 * 16 * 64 * 4;
+    static constexpr int TSH = RED;
+    static constexpr int LDS = 2 * STAGE > RED + BM * 4 ? 2 * STAGE : RED + BM * 4;
+    static_assert(KG == 2, "two k groups share the output tiles");
+    static constexpr int RA = 3;                          // A register sets (two steps ahead)
+    static constexpr int D = 3;                           // weight register sets (D steps ahead)
+    static constexpr int UNROLL = 6;
+    static_assert(UNROLL % RA == 0 && UNROLL % D == 0 && UNROLL % 2 == 0, "");
+    static_assert(2 * BN * KG == kThreads, "one half block per thread per step");
 };
 
-// One step's weight data of a thread: its half blocks' quants and scales.
-template <int UPT, int QW>
+// One step's weight data of a thread: its half block's quants and scale.
+template <int QW>
 struct WSet {
-    uint32_t q[UPT][QW];
-    uint32_t d[UPT];
+    uint32_t q[QW];
+    uint32_t d;
 };
 
 // Decode one half block into its two 16-byte B pieces (8 f16 weights each).
@@ -201,69 +269,62 @@ struct WSet {
 template <uint32_t WT, bool SF16, int QW>
 __device__ __forceinline__ void decode_half(const uint32_t (&q)[QW], f16x2 dh, float df, float mo,
                                             uint4& p0, uint4& p1) {
+    // the code bytes: Q4_0 nibbles (p0 from the low ones), Q8_0 q + 128
+    uint32_t c[4];
+    if constexpr (WT == kQ4) {
+        uint32_t mask = 0x0F0F0F0Fu;
+        asm("" : "+v"(mask));
+        c[0] = q[0] & mask;
+        c[1] = q[1] & mask;
+        c[2] = (q[0] >> 4) & mask;
+        c[3] = (q[1] >> 4) & mask;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = q[i] ^ 0x80808080u;
+    }
+    uint32_t o[8];
     if constexpr (SF16) {
         // f16 1024 + u from a code byte u by a byte permute, an exact f16
         // subtraction of 1024 + OFF, and one rounding in the multiply by d'
-        auto pair = [](uint32_t u, bool upper) {
-            return __builtin_amdgcn_perm(0x64646464u, u, upper ? 0x04030402u : 0x04010400u);
-        };
         const _Float16 off = static_cast<_Float16>(WT == kQ4 ? -1032.f : -1152.f);
         const f16x2 bias = {off, off};
-        auto w2 = [&](uint32_t u, bool upper) {
-            return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, pair(u, upper)) + bias) * dh);
-        };
-        if constexpr (WT == kQ4) {
-            uint32_t mask = 0x0F0F0F0Fu;
-            asm("" : "+v"(mask));
-            const uint32_t l0 = q[0] & mask, l1 = q[1] & mask;
-            const uint32_t h0 = (q[0] >> 4) & mask, h1 = (q[1] >> 4) & mask;
-            p0 = make_uint4(w2(l0, false), w2(l0, true), w2(l1, false), w2(l1, true));
-            p1 = make_uint4(w2(h0, false), w2(h0, true), w2(h1, false), w2(h1, true));
-        } else {
-            const uint32_t u0 = q[0] ^ 0x80808080u, u1 = q[1] ^ 0x80808080u;
-            const uint32_t u2 = q[2] ^ 0x80808080u, u3 = q[3] ^ 0x80808080u;
-            p0 = make_uint4(w2(u0, false), w2(u0, true), w2(u1, false), w2(u1, true));
-            p1 = make_uint4(w2(u2, false), w2(u2, true), w2(u3, false), w2(u3, true));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, c[i], 0x04010400u);
+            const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, c[i], 0x04030402u);
+            o[2 * i] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, lo) + bias) * dh);
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, hi) + bias) * dh);
         }
     } else {
         // fl32(u * d' - OFF * d') = fl32(v * d') in one fused operation, then
         // rounded to f16
-        auto w2 = [&](uint32_t u, bool upper) {
-            const float a = upper ? ubyte_f32<2>(u) : ubyte_f32<0>(u);
-            const float b = upper ? ubyte_f32<3>(u) : ubyte_f32<1>(u);
-            const f16x2 h = {static_cast<_Float16>(fmaf(a, df, mo)), static_cast<_Float16>(fmaf(b, df, mo))};
-            return __builtin_bit_cast(uint32_t, h);
-        };
-        if constexpr (WT == kQ4) {
-            uint32_t mask = 0x0F0F0F0Fu;
-            asm("" : "+v"(mask));
-            const uint32_t l0 = q[0] & mask, l1 = q[1] & mask;
-            const uint32_t h0 = (q[0] >> 4) & mask, h1 = (q[1] >> 4) & mask;
-            p0 = make_uint4(w2(l0, false), w2(l0, true), w2(l1, false), w2(l1, true));
-            p1 = make_uint4(w2(h0, false), w2(h0, true), w2(h1, false), w2(h1, true));
-        } else {
-            const uint32_t u0 = q[0] ^ 0x80808080u, u1 = q[1] ^ 0x80808080u;
-            const uint32_t u2 = q[2] ^ 0x80808080u, u3 = q[3] ^ 0x80808080u;
-            p0 = make_uint4(w2(u0, false), w2(u0, true), w2(u1, false), w2(u1, true));
-            p1 = make_uint4(w2(u2, false), w2(u2, true), w2(u3, false), w2(u3, true));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f16x2 a = {static_cast<_Float16>(fmaf(ubyte_f32<0>(c[i]), df, mo)),
+                             static_cast<_Float16>(fmaf(ubyte_f32<1>(c[i]), df, mo))};
+            const f16x2 b = {static_cast<_Float16>(fmaf(ubyte_f32<2>(c[i]), df, mo)),
+                             static_cast<_Float16>(fmaf(ubyte_f32<3>(c[i]), df, mo))};
+            o[2 * i] = __builtin_bit_cast(uint32_t, a);
+            o[2 * i + 1] = __builtin_bit_cast(uint32_t, b);
         }
     }
+    p0 = make_uint4(o[0], o[1], o[2], o[3]);
+    p1 = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <uint32_t WT, bool SF16, int NT, int WMW>
+template <uint32_t WT, bool SF16>
 __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ d, const int32_t* __restrict__ rexp,
     const uint4* __restrict__ xs, const int32_t* __restrict__ tshift, float* __restrict__ out,
     uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_n, uint32_t tiles_m, uint32_t kb_split) {
-    using C = Cfg<WT, NT, WMW>;
-    constexpr int KG = C::KG, UPT = C::UPT, QW = C::QW;
-    constexpr uint32_t SB = SF16 ? 2 : 4;
-    constexpr uint32_t BLK_Q = WT == kQ4 ? 16 : 32;  // quant bytes per block
+    using C = Cfg<WT, SF16>;
+    constexpr int NT = C::NT, KG = C::KG, QW = C::QW, RA = C::RA, D = C::D;
+    constexpr uint32_t SB = C::SB, BLK_Q = C::BLK_Q;
     __shared__ __attribute__((aligned(16))) uint8_t lds[C::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid % WMW, kg = wid / WMW;
+    const int wm = wid % C::WM, kg = wid / C::WM;
 
     // launch index -> tile: each XCD (launch index mod 8) gets a contiguous
     // run of tile indexes L = (split * tiles_m + tile_m) * tiles_n + tile_n
@@ -276,7 +337,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     const uint32_t kb0 = split * kb_split;
     const uint32_t kbe = min(KB, kb0 + kb_split);
     const uint32_t S = (kbe - kb0 + KG - 1) / KG;  // steps
-    const uint32_t MT = (M + 15) / 16;             // staged token tiles
+    const uint32_t MT = (M + kTokensPerTile - 1) / kTokensPerTile;  // staged token tiles
+    // (offsets of token tiles past MT stay below 2^32: MT * KB * 2048 < 2^31)
 
     // weights: buffers over this tile's rows
     const uint32_t row_bytes = WT == kQ4 ? K / 2 : K;
@@ -284,132 +346,135 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     const __amdgpu_buffer_rsrc_t qr = rsrc(q + static_cast<uint64_t>(n0) * row_bytes, nrows * row_bytes);
     const __amdgpu_buffer_rsrc_t dr =
         rsrc(static_cast<const uint8_t*>(d) + static_cast<uint64_t>(n0) * KB * SB, nrows * KB * SB);
-    const __amdgpu_buffer_rsrc_t xr = rsrc(xs, MT * KB * 1024);
+    const __amdgpu_buffer_rsrc_t xr = rsrc(xs, MT * KB * 2048);
 
-    // this thread's half blocks: unit u = ((j * KG + b) * 2 + h) * 16 + rr
-    // (units past the last get no data and write to the dummy slot)
-    uint32_t uq[UPT], ud[UPT], ub[UPT];
-    uint32_t lds_lo[UPT], lds_hi[UPT];
-    bool uok[UPT], udummy[UPT];
-    int ushift[UPT];
-#pragma unroll
-    for (int p = 0; p < UPT; ++p) {
-        const uint32_t u = tid + kThreads * p;
-        const uint32_t rr = u & 15, h = (u >> 4) & 1, b = (u >> 5) % KG, j = (u >> 5) / KG;
-        const uint32_t r = 16 * j + rr;
-        udummy[p] = u >= static_cast<uint32_t>(C::UNITS);
-        uok[p] = !udummy[p] && r < nrows;
-        uq[p] = r * row_bytes + (WT == kQ4 ? 8 : 16) * h;
-        ud[p] = r * KB * SB;
-        ub[p] = b;
-        const uint32_t g0 = WT == kQ4 ? h : 2 * h, g1 = WT == kQ4 ? 2 + h : 2 * h + 1;
-        const uint32_t frag = (b * NT + (j < NT ? j : 0)) * 1024;
-        lds_lo[p] = frag + (16 * g0 + rr) * 16;
-        lds_hi[p] = frag + (16 * g1 + rr) * 16;
-        ushift[p] = uok[p] ? kWeightTop - rexp[n0 + r] : 0;
-    }
+    // ---- this thread's half block of every step: row r = tid / 4, block
+    // b = (tid / 2) % 2 of the step, half h = tid % 2.  Four consecutive
+    // lanes read one row's 2 blocks (the address units serve such loads
+    // about four times faster than loads whose consecutive lanes are in
+    // different rows). ----
+    const uint32_t ur = tid >> 2, ub = (tid >> 1) & 1, uh = tid & 1;
+    const uint32_t uj = ur >> 5, un = ur & 31;
+    const bool uok = ur < nrows;
+    const uint32_t uq = ur * row_bytes + (WT == kQ4 ? 8 : 16) * uh;
+    const uint32_t ud = ur * KB * SB;
+    // pieces (slice s, lane half hh): Q4_0 low nibbles (0, h), high (1, h);
+    // Q8_0 (h, 0) and (h, 1)
+    const uint32_t us0 = WT == kQ4 ? 0 : uh, uh0 = WT == kQ4 ? uh : 0;
+    const uint32_t us1 = WT == kQ4 ? 1 : uh, uh1 = WT == kQ4 ? uh : 1;
+    const uint32_t lds_lo = frag_off(ub, (ub * 2 + us0) * NT + uj, 32 * uh0 + un);
+    const uint32_t lds_hi = frag_off(ub, (ub * 2 + us1) * NT + uj, 32 * uh1 + un);
+    const int ushift = uok ? kWeightTop - rexp[n0 + ur] : 0;
+    // the tile's token shifts (zero past the last token), kept for the end
+    const uint32_t mrows = min(static_cast<uint32_t>(C::BM), M - m0);
+    const int32_t tsh_mine = tid < C::BM
+        ? static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(rsrc(tshift + m0, mrows * 4), tid * 4, 0, 0))
+        : 0;
 
-    auto load_w = [&](uint32_t s, WSet<UPT, QW>& w) {
+    auto load_w = [&](uint32_t s, WSet<QW>& w) {
+        const uint32_t kb = kb0 + s * KG + ub;
+        const bool ok = uok && kb < kbe;
+        const uint32_t qo = ok ? uq + kb * BLK_Q : kOob;
+        const uint32_t dof = ok ? ud + kb * SB : kOob;
+        if constexpr (WT == kQ4) {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(qr, qo, 0, 0);
+            w.q[0] = v[0];
+            w.q[1] = v[1];
+        } else {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qr, qo, 0, 0);
 #pragma unroll
-        for (int p = 0; p < UPT; ++p) {
-            const uint32_t kb = kb0 + s * KG + ub[p];
-            const bool ok = uok[p] && kb < kbe;
-            const uint32_t qo = ok ? uq[p] + kb * BLK_Q : kOob;
-            const uint32_t dof = ok ? ud[p] + kb * SB : kOob;
-            if constexpr (WT == kQ4) {
-                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(qr, qo, 0, 0);
-                w.q[p][0] = v[0];
-                w.q[p][1] = v[1];
-            } else {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(qr, qo, 0, 0);
+            for (int i = 0; i < 4; ++i) w.q[i] = v[i];
+        }
+        if constexpr (SF16) w.d = __builtin_amdgcn_raw_buffer_load_b16(dr, dof, 0, 0);
+        else w.d = __builtin_amdgcn_raw_buffer_load_b32(dr, dof, 0, 0);
+    };
+    auto decode = [&](const WSet<QW>& w, uint32_t stage) {
+        const float dv = __builtin_amdgcn_ldexpf(scale_from_bits<SF16>(w.d), ushift);
+        const _Float16 dh = static_cast<_Float16>(dv);
+        uint4 p0, p1;
+        decode_half<WT, SF16, QW>(w.q, f16x2{dh, dh}, dv, (WT == kQ4 ? -8.f : -128.f) * dv, p0, p1);
+        *reinterpret_cast<uint4*>(lds + stage + lds_lo) = p0;
+        *reinterpret_cast<uint4*>(lds + stage + lds_hi) = p1;
+    };
+
+    // ---- A operands: token tiles 2 wm, 2 wm + 1 of the tile, both slices of
+    // block kg of step s.  No condition guards these loads (a condition
+    // here becomes a branch whose other side drains every outstanding
+    // load): a block past the slice is taken from the same token's row,
+    // clamped to its last block, and meets weights of zero (the weight loads
+    // past the slice return zeros); a token tile past the staged ones lies
+    // past the buffer's end and reads zeros. ----
+    const uint32_t mt0 = tile_m * (C::BM / kTokensPerTile) + 2 * wm;
+    auto load_a = [&](uint32_t s, f16x8 (&a)[2][2]) {
+        const uint32_t kb = min(kb0 + s * KG + kg, KB - 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w.q[p][i] = v[i];
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                const uint32_t off = ((((mt0 + i) * KB + kb) * 2 + sl) * 64 + lane) * 16;
+                a[sl][i] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
             }
-            if constexpr (SF16) w.d[p] = __builtin_amdgcn_raw_buffer_load_b16(dr, dof, 0, 0);
-            else w.d[p] = __builtin_amdgcn_raw_buffer_load_b32(dr, dof, 0, 0);
-        }
     };
-    auto decode = [&](const WSet<UPT, QW>& w, uint32_t stage) {
+    f32x16 acc[2][NT];
 #pragma unroll
-        for (int p = 0; p < UPT; ++p) {
-            const float dv = __builtin_amdgcn_ldexpf(scale_from_bits<SF16>(w.d[p]), ushift[p]);
-            const _Float16 dh = static_cast<_Float16>(dv);
-            uint4 p0, p1;
-            decode_half<WT, SF16, QW>(w.q[p], f16x2{dh, dh}, dv, (WT == kQ4 ? -8.f : -128.f) * dv,
-                                      p0, p1);
-            const uint32_t lo = udummy[p] ? C::DUMMY + (lds_lo[p] & 1023) : stage + lds_lo[p];
-            const uint32_t hi = udummy[p] ? C::DUMMY + (lds_hi[p] & 1023) : stage + lds_hi[p];
-            *reinterpret_cast<uint4*>(lds + lo) = p0;
-            *reinterpret_cast<uint4*>(lds + hi) = p1;
-        }
-    };
-    // A operands: token tiles 4 wm .. 4 wm + 3 of the tile, block kg of step s
-    const uint32_t mt0 = tile_m * (C::BM / 16) + 4 * wm;
-    auto load_a = [&](uint32_t s, f16x8 (&a)[4]) {
-        const uint32_t kb = kb0 + s * KG + kg;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t mt = mt0 + i;
-            const uint32_t off = (kb < kbe && mt < MT) ? ((mt * KB + kb) * 64 + lane) * 16 : kOob;
-            a[i] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-        }
-    };
-    f32x4 acc[4][NT];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](uint32_t stage, const f16x8 (&a)[4]) {
-        const uint8_t* bs = lds + stage + kg * NT * 1024 + lane * 16;
-        f16x8 b[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const f16x8*>(bs + j * 1024);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    };
-    // Instruction order of a step (a hint to the scheduler, which otherwise
-    // sinks the loads to the end of the step and the decode after every
-    // matrix-core product): the step's loads first, then the products, two
-    // B reads ahead, with the decode's vector instructions and LDS writes
-    // placed between them.
-    constexpr int kLoads = 4 + UPT * 2;
-    auto order = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x020, kLoads, 0);  // buffer loads
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // B reads 0, 1
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    auto compute = [&](uint32_t stage, const f16x8 (&a)[2][2]) {
+        const uint8_t* bs = lds + stage;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
+        for (int sl = 0; sl < 2; ++sl) {
+            f16x8 bf[NT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two vector ops
-            }
-            if (j + 2 < NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int j = 0; j < NT; ++j)
+                bf[j] = *reinterpret_cast<const f16x8*>(bs + frag_off(kg, (kg * 2 + sl) * NT + j, lane));
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[sl][i], bf[j], acc[i][j], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x200, 2 * UPT, 0);  // decoded pieces
+    };
+    // Instruction order within a step (a hint to the scheduler, which would
+    // otherwise bunch the decode after the products): B reads two ahead of
+    // the products that use them, the decode's vector instructions between
+    // the products.
+    auto order = [&]() {
+        constexpr int NMF = 2 * NT * 2;                          // products per step
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // B reads
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one product
+            if (k % 2 == 0 && k / 2 + 2 < 2 * NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // vector ops
+        }
     };
 
-    constexpr int D = C::DEPTH;
-    WSet<UPT, QW> w[D];
-    f16x8 a[2][4];
+    constexpr uint32_t ST0 = 0, ST1 = C::STAGE;
+    WSet<QW> w[D];
+    f16x8 a[RA][2][2];
+#pragma unroll
+    for (int k = 0; k < RA - 1; ++k) load_a(k, a[k]);
 #pragma unroll
     for (int k = 0; k < D; ++k) load_w(k, w[k]);
-    load_a(0, a[0]);
-    decode(w[0], 0);
+    decode(w[0], ST0);
     __syncthreads();
-    // step s: A operands of step s + 1 and weights of step s + D are
-    // requested, step s is multiplied from LDS stage s & 1, and the weights
-    // of step s + 1 are decoded into the other stage.  The last step decodes
-    // (zeros) into the unused stage.  Four steps per iteration, so that
-    // every register set is named at compile time.
+    // step s: the A operands of step s + RA - 1, then the weights of step
+    // s + D, are requested (in that order, so that the activations never
+    // wait behind a weight load issued in the same step), step s is
+    // multiplied from LDS stage s & 1, and the weights of step s + 1 are
+    // decoded into the other stage.  The last step decodes (zeros) into the
+    // unused stage.
     uint32_t s = 0;
 #define QMV_STEP(K_)                                                \
-    load_a(s + 1, a[((K_) + 1) & 1]);                               \
+    load_a(s + RA - 1, a[((K_) + RA - 1) % RA]);                    \
+    __builtin_amdgcn_sched_barrier(0);                              \
     load_w(s + D, w[(K_) % D]);                                     \
-    compute(((K_) & 1) * C::STAGE, a[(K_) & 1]);                    \
-    decode(w[((K_) + 1) % D], (((K_) + 1) & 1) * C::STAGE);         \
+    __builtin_amdgcn_sched_barrier(0);                              \
+    compute((K_) & 1 ? ST1 : ST0, a[(K_) % RA]);                    \
+    decode(w[((K_) + 1) % D], (K_) & 1 ? ST0 : ST1);                \
     order();                                                        \
     __syncthreads();                                                \
     if (++s >= S) break;
@@ -418,71 +483,67 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
         QMV_STEP(1)
         QMV_STEP(2)
         QMV_STEP(3)
+        QMV_STEP(4)
+        QMV_STEP(5)
     }
 #undef QMV_STEP
 
-    // ---- the k groups' sums meet in LDS (the stages are free now) ----
-    if constexpr (KG > 1) {
-        float* red = reinterpret_cast<float*>(lds);
+    // ---- the k groups' sums meet in LDS: k group 0 finishes row tiles 0
+    // and 1, k group 1 tiles 2 and 3; each hands the other pair to its
+    // partner wave ----
+    float* red = reinterpret_cast<float*>(lds);
+    int32_t* tsl = reinterpret_cast<int32_t*>(lds + C::TSH);
+    auto hand = [&](auto JO) {
+        constexpr int jo = decltype(JO)::value;
 #pragma unroll
-        for (int j0 = 0; j0 < NT; j0 += C::JR) {
-            if (kg > 0) {
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int jj = 0; jj < C::JR; ++jj)
-                    if (j0 + jj < NT)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                red[((((jj * (KG - 1) + kg - 1) * WMW + wm) * 4 + i) * 4 + v) * 64 + lane] =
-                                    acc[i][j0 + jj][v];
-            }
-            __syncthreads();
-            if (kg == 0) {
-#pragma unroll
-                for (int jj = 0; jj < C::JR; ++jj)
-                    if (j0 + jj < NT)
-#pragma unroll
-                        for (int gg = 1; gg < KG; ++gg)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                                for (int v = 0; v < 4; ++v)
-                                    acc[i][j0 + jj][v] +=
-                                        red[((((jj * (KG - 1) + gg - 1) * WMW + wm) * 4 + i) * 4 + v) * 64 + lane];
-            }
-            __syncthreads();
-        }
-        if (kg > 0) return;
-    }
+                for (int v = 0; v < 16; ++v)
+                    red[((((kg * C::WM + wm) * 2 + jj) * 2 + i) * 16 + v) * 64 + lane] = acc[i][jo + jj][v];
+    };
+    if (kg == 0) hand(std::integral_constant<int, 2>{});
+    else hand(std::integral_constant<int, 0>{});
+    if (tid < C::BM) tsl[tid] = tsh_mine;
+    __syncthreads();
 
-    // ---- epilogue: lane holds row n = lane % 16 of each 16x16 tile and
-    // tokens 4 (lane / 16) + v; outputs scaled back by powers of two ----
-    float* o = out + static_cast<uint64_t>(split) * M * N;
-    const uint32_t mw = m0 + 64 * wm + 4 * (lane >> 4);
-    int tsh[4][4];
+    // ---- epilogue: lane holds row n = lane % 32 of each 32x32 tile and
+    // tokens 8 (v / 4) + 4 (lane / 32) + v % 4; outputs scaled back by
+    // powers of two and stored through a buffer over the tile's tokens
+    // (stores past the last token or row are dropped) ----
+    const uint32_t mw = 64 * wm + 4 * (lane >> 5);  // first token, tile-relative
+    int4 ts[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const uint32_t m = mw + 16 * i + v;
-            tsh[i][v] = m < M ? tshift[m] : 0;
+        for (int g4 = 0; g4 < 4; ++g4) ts[i][g4] = *reinterpret_cast<const int4*>(tsl + mw + 32 * i + 8 * g4);
+    const __amdgpu_buffer_rsrc_t orr =
+        rsrc(out + (static_cast<uint64_t>(split) * M + m0) * N + n0, mrows * N * 4);
+    const __amdgpu_buffer_rsrc_t er = rsrc(rexp + n0, nrows * 4);
+    auto finish = [&](auto JK) {
+        constexpr int jk = decltype(JK)::value;
+        const int partner = (1 - kg) * C::WM + wm;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t nl = 32 * (jk + jj) + (lane & 31);  // tile-relative row
+            const int rsh = kWeightTop - static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(er, nl * 4, 0, 0));
+            const uint32_t ob = nl < nrows ? nl * 4 : kOob;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float sum = acc[i][jk + jj][v] + red[(((partner * 2 + jj) * 2 + i) * 16 + v) * 64 + lane];
+                    const int t = ts[i][v >> 2][v & 3];
+                    const uint32_t ml = mw + 32 * i + 8 * (v >> 2) + (v & 3);
+                    const uint32_t off = nl < nrows ? ml * N * 4 + ob : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(sum, -(rsh + t))), orr, off, 0, 0);
+                }
         }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const uint32_t n = n0 + 16 * j + (lane & 15);
-        if (n >= N) continue;
-        const int rsh = kWeightTop - rexp[n];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t m = mw + 16 * i + v;
-                if (m < M)
-                    o[static_cast<uint64_t>(m) * N + n] =
-                        __builtin_amdgcn_ldexpf(acc[i][j][v], -(rsh + tsh[i][v]));
-            }
-    }
+    };
+    if (kg == 0) finish(std::integral_constant<int, 0>{});
+    else finish(std::integral_constant<int, 2>{});
 }
 
 // y = sum of the split-K partials, in slice order (deterministic).  Slice z
@@ -520,14 +581,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // Largest batch of one staged pass: the staged activations (2 bytes per
 // value) stay within 32-bit buffer offsets.
 uint32_t pass_tokens(uint32_t cols) {
-    const uint64_t per_tile = uint64_t{16} * cols * 2;
+    const uint64_t per_tile = uint64_t{kTokensPerTile} * cols * 2;
     uint64_t tiles = (uint64_t{0x7FFFFFFF}) / per_tile;
     if (tiles > (1u << 20)) tiles = 1u << 20;
-    return static_cast<uint32_t>(tiles * 16);
+    return static_cast<uint32_t>(tiles * kTokensPerTile);
 }
 
 struct Plan {
-    int nt = 8, wmw = 4;            // row tiles of 16 per workgroup, token waves of 64
     uint32_t tiles_n = 0, tiles_m = 0, splits = 1, kb_split = 0;
     uint32_t pass = 0;              // tokens per staged pass
 };
@@ -536,70 +596,34 @@ Plan make_plan(const MatView& m, uint32_t batch) {
     Plan p;
     p.pass = batch < pass_tokens(m.cols) ? batch : pass_tokens(m.cols);
     const uint32_t M = p.pass;
-    p.wmw = M <= 64 ? 1 : M <= 128 ? 2 : 4;
-    const uint32_t bm = 64u * p.wmw, kg = 8u / p.wmw;
+    constexpr uint32_t bm = 256, kg = 2;
     p.tiles_m = (M + bm - 1) / bm;
+    p.tiles_n = (m.rows + 127) / 128;
     const uint32_t KB = m.cols / 32;
     const uint32_t steps = (KB + kg - 1) / kg;
-    // Row tiles of 128 or 112 rows, whichever leaves fewer compute units
-    // idle over the launch's rounds of 256 workgroups (14336 rows: 128 tiles
-    // of 112 rows fill two token tiles' 256 workgroups exactly); then K is
-    // split while the tiles are too few and every slice keeps >= 8 steps.
-    // (batches of at most 64 take 112-row tiles only: at 128 rows, with four
-    // half blocks to decode per thread, the kernel runs out of registers)
-    double best = -1.0;
-    for (int nt : {8, 7}) {
-        if (p.wmw == 1 && nt == 8) continue;
-        const uint32_t bn = 16u * nt;
-        const uint32_t tn = (m.rows + bn - 1) / bn;
-        uint32_t splits = 1;
-        while (uint64_t{tn} * p.tiles_m * splits * 2 <= 320 && steps / (splits * 2) >= 8) splits *= 2;
-        const uint64_t wgs = uint64_t{tn} * p.tiles_m * splits;
-        const uint64_t rounds = (wgs + 255) / 256;
-        const double eff = static_cast<double>(m.rows) / (static_cast<double>(tn) * bn) *
-                           static_cast<double>(wgs) / static_cast<double>(rounds * 256);
-        if (eff > best + 1e-9) {
-            best = eff;
-            p.nt = nt;
-            p.tiles_n = tn;
-            p.splits = splits;
-        }
-    }
-    const uint32_t per = (steps + p.splits - 1) / p.splits;
+    // too few tiles for 256 compute units: split K, keeping >= 8 steps a slice
+    uint32_t splits = 1;
+    while (uint64_t{p.tiles_n} * p.tiles_m * splits * 2 <= 320 && steps / (splits * 2) >= 8) splits *= 2;
+    const uint32_t per = (steps + splits - 1) / splits;
     p.kb_split = per * kg;
     p.splits = (KB + p.kb_split - 1) / p.kb_split;
     return p;
 }
 
 uint64_t staged_bytes(uint32_t tokens, uint32_t cols) {
-    const uint64_t mp = (uint64_t{tokens} + 15) / 16 * 16;
+    const uint64_t mp = (uint64_t{tokens} + kTokensPerTile - 1) / kTokensPerTile * kTokensPerTile;
     return mp * cols * 2 + ((mp * 4 + 255) & ~uint64_t{255});
 }
 
-template <uint32_t WT, bool SF16, int NT, int WMW>
+template <uint32_t WT, bool SF16>
 hipError_t launch_mm(const MatView& m, const uint4* xs, const int32_t* tsh, float* out,
                      uint32_t M, const Plan& p, hipStream_t s) {
     const uint64_t nwg = uint64_t{p.tiles_n} * p.tiles_m * p.splits;
     if (nwg > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mm::gemm_f16_kernel<WT, SF16, NT, WMW>), dim3(static_cast<uint32_t>(nwg)),
+    hipLaunchKernelGGL((mm::gemm_f16_kernel<WT, SF16>), dim3(static_cast<uint32_t>(nwg)),
                        dim3(mm::kThreads), 0, s, m.q, m.d, m.rexp, xs, tsh, out, M, m.rows, m.cols,
                        p.tiles_n, p.tiles_m, p.kb_split);
     return hipGetLastError();
-}
-
-template <uint32_t WT, bool SF16>
-hipError_t launch_mm_shape(const MatView& m, const uint4* xs, const int32_t* tsh, float* out,
-                           uint32_t M, const Plan& p, hipStream_t s) {
-#define QMV_MM(NT_, WMW_) \
-    if (p.nt == NT_ && p.wmw == WMW_) return launch_mm<WT, SF16, NT_, WMW_>(m, xs, tsh, out, M, p, s);
-    QMV_MM(8, 4)
-    QMV_MM(7, 4)
-    QMV_MM(8, 2)
-    QMV_MM(7, 2)
-    QMV_MM(8, 1)
-    QMV_MM(7, 1)
-#undef QMV_MM
-    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -640,13 +664,18 @@ size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool /*x_f32*/) {
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y, uint32_t batch,
                        void* workspace, hipStream_t s) {
     if (workspace == nullptr) return hipErrorInvalidValue;
+    // the scale array is addressed through one 32-bit buffer range, and so
+    // is a tile's 256 tokens of output
+    if (uint64_t{m.rows} * (m.cols / 32) * (m.scale_f16 ? 2 : 4) >= 0xFFFFFFF0ull ||
+        uint64_t{m.rows} * 256 * 4 >= 0xFFFFFFF0ull)
+        return hipErrorNotSupported;
     const Plan p0 = make_plan(m, batch);
     if (p0.pass == 0) return hipErrorInvalidValue;
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     for (uint32_t done = 0; done < batch;) {
         const uint32_t M = batch - done < p0.pass ? batch - done : p0.pass;
         const Plan p = M == p0.pass ? p0 : make_plan(m, M);
-        const uint64_t mp = (uint64_t{M} + 15) / 16 * 16;
+        const uint64_t mp = (uint64_t{M} + kTokensPerTile - 1) / kTokensPerTile * kTokensPerTile;
         uint4* xs = reinterpret_cast<uint4*>(ws);
         int32_t* tsh = reinterpret_cast<int32_t*>(ws + mp * m.cols * 2);
         float* part = reinterpret_cast<float*>(ws + staged_bytes(p0.pass, m.cols));
@@ -663,11 +692,11 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y, ui
         if (e != hipSuccess) return e;
         float* out = p.splits > 1 ? part : yp;
         if (m.wtype == kQ4)
-            e = m.scale_f16 ? launch_mm_shape<kQ4, true>(m, xs, tsh, out, M, p, s)
-                            : launch_mm_shape<kQ4, false>(m, xs, tsh, out, M, p, s);
+            e = m.scale_f16 ? launch_mm<kQ4, true>(m, xs, tsh, out, M, p, s)
+                            : launch_mm<kQ4, false>(m, xs, tsh, out, M, p, s);
         else
-            e = m.scale_f16 ? launch_mm_shape<kQ8, true>(m, xs, tsh, out, M, p, s)
-                            : launch_mm_shape<kQ8, false>(m, xs, tsh, out, M, p, s);
+            e = m.scale_f16 ? launch_mm<kQ8, true>(m, xs, tsh, out, M, p, s)
+                            : launch_mm<kQ8, false>(m, xs, tsh, out, M, p, s);
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
             e = launch_splitk_sum(part, yp, uint64_t{M} * m.rows, p.splits, s);

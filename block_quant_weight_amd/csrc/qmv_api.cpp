@@ -244,7 +244,9 @@ int qmv_gemv(qmv_handle h, const float* x, float* y, uint32_t batch,
     void* ws = nullptr;
     st = workspace_for(s, qmv::gemv_workspace_bytes(v, batch), &ws);
     if (st != QMV_OK) return st;
-    return device_status(qmv::launch_gemv(v, x, y, batch, ws, s));
+    const hipError_t e = qmv::launch_gemv(v, x, y, batch, ws, s);
+    if (e == hipErrorNotSupported) return QMV_E_SHAPE;
+    return device_status(e);
 }
 
 int qmv_gemv_group(const qmv_handle* hs, uint32_t n, const float* x, float* const* ys,
@@ -297,7 +299,9 @@ int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
     void* ws = nullptr;
     st = workspace_for(s, qmv::gemm_workspace_bytes(v, batch, false), &ws);
     if (st != QMV_OK) return st;
-    return device_status(qmv::launch_gemm(v, x_bf16, false, y, batch, ws, s));
+    const hipError_t e = qmv::launch_gemm(v, x_bf16, false, y, batch, ws, s);
+    if (e == hipErrorNotSupported) return QMV_E_SHAPE;
+    return device_status(e);
 }
 
 int qmv_gemm_q8(qmv_handle h, const int8_t* xq, const float* dx, float* y, uint32_t batch,
