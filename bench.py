@@ -7,20 +7,32 @@ block_quant_weight_amd.synth).  The weights of successive steps rotate over
 enough byte-identical copies (>= 512 MB in total) that neither the 256 MB
 MALL nor the L2 can serve them: every step reads its weights from HBM.  The
 timed steps run as one captured HIP graph (launch overhead out of the way),
-bracketed by device synchronisation and HIP events on the launching stream.
+after the graph has been replayed for at least --warm-seconds (so that the
+GPU clock has left its idle state), bracketed by device synchronisation and
+HIP events on the launching stream.
 
-Default workload: Q4_0 GEMV, 4096 x 4096, f16 scales, batch 1.  Other
-workloads (--workload): q8_gemv_512, decode_layer (wq|wk|wv and w1|w3 grouped
-on their shared inputs), decode_layer_gated (the same, with w1|w3 as one gated
-launch, SiLU(w1 x) * (w3 x), whose output is w2's input), decode_layer_7 (one
-launch per matrix), gemm_q4_14336x4096,
-gemm_q8_4096x14336, lm_head_b1, lm_head_b64, embed_64, writer_q4_14336x4096
-(the weight writer: float32 weights to a Q4_0 f16-scale image by the round
-rule), writer_q4_search_14336x4096 (the same by the least-squares search,
+Default (no --workload): the five configurations in one process, one JSON
+line whose headline is the shared-classifier LM head at batch 1 (the largest
+single-GPU workload) and whose "configs" object holds every workload's rate,
+step time, roofline and oracle baseline:
+  q8_gemv_512         Q8_0 GEMV 512x512, f32 scales, batch 1
+  q4_gemv_4096        Q4_0 GEMV 4096x4096, f16 scales, batch 1
+  decode_layer        mixed Q4_0/Q8_0 decode layer (wq|wk|wv and w1|w3 grouped)
+  gemm_q4_14336x4096  prefill GEMM, Q4_0 f16 scales x bf16 [512x4096]
+  gemm_q8_4096x14336  prefill GEMM, Q8_0 f32 scales x bf16 [512x14336]
+  lm_head_b1/_b64     Q8_0 248320x1024 f16 scales as the LM head, batch 1 / 64
+  embed_64            dequantized gather of 64 rows of the same table
+Each GEMV workload also carries the read ceiling at its largest launch's byte
+count (a plain 16-byte-load read of that many bytes, qmv_read_probe).
+
+Other workloads (--workload): decode_layer_gated (w1|w3 as one gated launch,
+SiLU(w1 x) * (w3 x), whose output is w2's input), decode_layer_7 (one launch
+per matrix), writer_q4_14336x4096 (float32 weights to a Q4_0 f16-scale image
+by the round rule), writer_q4_search_14336x4096 (the least-squares search,
 bound by float32 arithmetic), gemm_q8act_q4_14336x4096 and
-gemm_q8act_q8_4096x14336 (the prefill shapes on the int8 path: float32
-activations quantized to Q8_0, then the int8 matrix-core product), and copy
-(a plain device copy, used to calibrate HBM byte counters).
+gemm_q8act_q8_4096x14336 (the prefill shapes on the int8 path), read_stream
+(the read ceiling over a range of sizes), and copy (a plain device copy, used
+to calibrate HBM byte counters).
 """
 from __future__ import annotations
 
@@ -38,8 +50,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Q4_0/Q8_0 GEMV effective GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
-INT8_PEAK_TOPS = 5000.0       # MI355X dense int8 MFMA, published
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16/f16 MFMA, published (2.4 GHz)
+INT8_PEAK_TOPS = 5033.2       # MI355X dense int8 MFMA, published (2.4 GHz)
 # plain float32 vector operations (multiply, add, round, clamp, each one
 # operation): the published 157.3 TFLOP/s counts a fused multiply-add as two,
 # and an unfused operation takes the same issue slot, so 157.3 / 2 per second
@@ -108,6 +120,8 @@ def workload(name):
                 [(0, Q8, 1, 248320, 1024)], 64)
     if name == "copy":
         return ("plain device copy of 256 MiB (counter calibration)", "copy", 0, [], 0)
+    if name == "read_stream":
+        return ("read ceiling: qmv_read_probe over a range of sizes", "read", 0, [], 0)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -126,8 +140,9 @@ DOMINANT_KERNEL = {
     "decode_layer_7": ("gemv_oneshot_kernel (w2)", "gemv.hip"),
     "lm_head_b1": ("gemv_oneshot_kernel", "gemv.hip"),
     "lm_head_b64": ("gemv_mfma_kernel (f16 operands)", "gemv_mfma.hip"),
-    "gemm_q4_14336x4096": ("gemm_big_kernel", "gemm.hip"),
-    "gemm_q8_4096x14336": ("gemm_big_kernel + splitk_reduce_kernel", "gemm.hip"),
+    "gemm_q4_14336x4096": ("qmv_gemm call: stage_x_kernel + gemm_f16_kernel", "gemm.hip"),
+    "gemm_q8_4096x14336": ("qmv_gemm call: stage_x_kernel + gemm_f16_kernel + "
+                           "splitk_reduce_kernel", "gemm.hip"),
     "gemm_q8act_q4_14336x4096": ("gemm_q8act_kernel", "gemm_i8.hip"),
     "gemm_q8act_q8_4096x14336": ("gemm_q8act_kernel + splitk_reduce_kernel", "gemm_i8.hip"),
     "embed_64": ("embed_kernel", "misc.hip"),
@@ -311,31 +326,13 @@ def cpu_baseline(kind, config, mats, batch, budget_s):
                       f"(f64, {threads} threads, {el:.1f} s)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="q4_gemv_4096")
-    ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(the product runs on a single MI355X; see the sharding notes)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args, stream, cpu_budget):
+    """Times one workload; returns its JSON record (the printed line's fields)."""
     import torch
     from block_quant_weight_amd import qmv as Q
     from block_quant_weight_amd import synth
 
-    desc, kind, config, mats, batch = workload(args.workload)
-    torch.cuda.set_device(0)
-    # One side stream for warm-up, capture and timing: the library keeps its
-    # split-K workspace per stream, so the capture stream must be warmed up.
-    stream = torch.cuda.Stream()
-    torch.cuda.set_stream(stream)
+    desc, kind, config, mats, batch = workload(name)
 
     if kind == "copy":
         n = 256 << 20
@@ -351,16 +348,16 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / 10
-        print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n,
-                          "ms_per_copy": ms, "GB/s": 2 * n / ms / 1e6}))
-        return
+        return {"workload": "copy", "bytes_read": n, "bytes_written": n,
+                "ms_per_copy": ms, "GB/s": 2 * n / ms / 1e6}
 
     if kind == "writer":
-        run_writer(args, desc, config, mats, stream)
-        return
+        return run_writer(args, name, desc, config, mats, stream, cpu_budget)
+    if kind == "read":
+        return read_stream(args, stream)
 
-    groups = launch_groups(args.workload, mats)
-    gated = args.workload == "decode_layer_gated"
+    groups = launch_groups(name, mats)
+    gated = name == "decode_layer_gated"
     step_bytes, step_flops = step_work(kind, mats, batch, groups if kind == "gemv" else None,
                                        gated)
     set_bytes = sum(matrix_bytes(wt, sf, r, c) for _, wt, sf, r, c in mats)
@@ -369,7 +366,7 @@ def main():
         ncopies = 1   # a gather touches 64 rows; rows are drawn afresh per step
     steps = args.steps if args.steps is not None else (200 if kind in ("gemm", "gemm_q8") else 1000)
     warmup = args.warmup if args.warmup is not None else 20
-    log(f"workload {args.workload}: {desc}; {ncopies} weight copies; "
+    log(f"workload {name}: {desc}; {ncopies} weight copies; "
         f"{steps} steps after {warmup} warm-up")
 
     imgs = {m: make_image(config, m, wt, sf, r, c) for (m, wt, sf, r, c) in mats}
@@ -437,31 +434,9 @@ def main():
             else:
                 Q.qmv_embed_rows(h, id_sets[i % len(id_sets)], out)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
     use_graph = not args.no_graph
-    if use_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(steps):
-                step(warmup + i)
-        g.replay()                        # untimed: first replay uploads the graph
-        torch.cuda.synchronize()
-    log("warm-up done")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    if use_graph:
-        g.replay()
-    else:
-        for i in range(steps):
-            step(warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    ms_step = ms / steps
-    log(f"timed {steps} steps: {ms:.3f} ms")
+    ms_step = timed_steps(step, steps, warmup, stream, use_graph, args.warm_seconds)
+    log(f"timed {steps} steps: {ms_step * steps:.3f} ms")
 
     launches_per_step = len(groups) if kind == "gemv" else len(mats)
     if kind == "gemm":
@@ -481,52 +456,43 @@ def main():
     # step it is the step; otherwise that launch alone is timed again the same
     # way (rotated copies, one captured graph, events on the launch stream).
     if kind == "gemv" and len(groups) > 1:
-        dom = max(range(len(groups)),
-                  key=lambda k: sum(matrix_bytes(*mats[j][1:]) for j in groups[k]))
-        gr = groups[dom]
-        dom_bytes, _ = step_work(kind, [mats[j] for j in gr], batch, [list(range(len(gr)))],
-                                 gated)
-        # this launch rotates over its own >= 512 MB of copies: the step's
-        # copies plus extra uploads of the group's matrices
-        dom_set = sum(matrix_bytes(*mats[j][1:]) for j in gr)
-        dom_copies = max(ncopies, -(-ROTATE_BYTES // dom_set))
-        dom_handles = [{j: handles[k][j] for j in gr} for k in range(ncopies)]
-        extra = []
-        for _ in range(dom_copies - ncopies):
-            hs = {}
-            for j in gr:
-                m, wt, sf, r, c = mats[j]
-                h = Q.qmv_create(wt, sf, r, c)
-                Q.qmv_upload(h, make_image(config, m, wt, sf, r, c), stream=stream)
-                hs[j] = h
-                extra.append(h)
-            dom_handles.append(hs)
+        # every launch of the step alone, each over its own >= 512 MB of
+        # copies (the step's copies plus extra uploads of its matrices)
+        per_launch = []
+        for gr in groups:
+            g_bytes, _ = step_work(kind, [mats[j] for j in gr], batch, [list(range(len(gr)))],
+                                   gated)
+            g_set = sum(matrix_bytes(*mats[j][1:]) for j in gr)
+            g_copies = max(ncopies, -(-ROTATE_BYTES // g_set))
+            g_handles = [{j: handles[k][j] for j in gr} for k in range(ncopies)]
+            extra = []
+            for _ in range(g_copies - ncopies):
+                hs = {}
+                for j in gr:
+                    m, wt, sf, r, c = mats[j]
+                    h = Q.qmv_create(wt, sf, r, c)
+                    Q.qmv_upload(h, make_image(config, m, wt, sf, r, c), stream=stream)
+                    hs[j] = h
+                    extra.append(h)
+                g_handles.append(hs)
 
-        def launch(i):
-            run_group(dom_handles[i % dom_copies], gr)
-        for i in range(warmup):
-            launch(i)
-        torch.cuda.synchronize()
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=stream):
-            for i in range(steps):
-                launch(warmup + i)
-        g2.replay()
-        torch.cuda.synchronize()
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e2.record(stream)
-        g2.replay()
-        e3.record(stream)
-        torch.cuda.synchronize()
-        dom_ms = e2.elapsed_time(e3) / steps
-        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-        log(f"largest launch (matrices {gr}) alone, {dom_copies} copies: "
-            f"{dom_ms * 1e3:.3f} us per launch")
-        for h in extra:
-            Q.qmv_destroy(h)
-        dom_desc = {"matrices": [LAYER[j][0] for j in gr] if args.workload.startswith("decode")
-                    else gr, "algorithmic_bytes_per_launch": dom_bytes,
-                    "us_per_launch": round(dom_ms * 1e3, 3), "copies_rotated": dom_copies}
+            def launch(i, gr=gr, g_handles=g_handles, g_copies=g_copies):
+                run_group(g_handles[i % g_copies], gr)
+            g_ms = timed_steps(launch, steps, warmup, stream, use_graph, args.warm_seconds)
+            for h in extra:
+                Q.qmv_destroy(h)
+            log(f"launch {[LAYER[j][0] for j in gr]} alone, {g_copies} copies: "
+                f"{g_ms * 1e3:.3f} us")
+            per_launch.append({"matrices": [LAYER[j][0] for j in gr] if name.startswith("decode")
+                               else gr, "algorithmic_bytes_per_launch": g_bytes,
+                               "us_per_launch": round(g_ms * 1e3, 3),
+                               "GB/s": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                               "copies_rotated": g_copies})
+        # the roofline's kernel: the largest launch
+        dom_desc = max(per_launch, key=lambda d: d["algorithmic_bytes_per_launch"])
+        achieved = dom_desc["GB/s"]
+        dom_desc = dict(dom_desc)
+        dom_desc["every_launch"] = per_launch
     elif kind == "gemm_q8":
         # the int8 product alone (its activations quantized once, before the
         # graph), the same rotation and timing
@@ -536,21 +502,7 @@ def main():
 
         def launch(i):
             Q.qmv_gemm_q8(handles[i % ncopies][0], xqs[0], dxs[0], ys[0])
-        for i in range(warmup):
-            launch(i)
-        torch.cuda.synchronize()
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=stream):
-            for i in range(steps):
-                launch(warmup + i)
-        g2.replay()
-        torch.cuda.synchronize()
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e2.record(stream)
-        g2.replay()
-        e3.record(stream)
-        torch.cuda.synchronize()
-        dom_ms = e2.elapsed_time(e3) / steps
+        dom_ms = timed_steps(launch, steps, warmup, stream, use_graph, args.warm_seconds)
         achieved = step_flops / (dom_ms * 1e-3) / 1e12
         log(f"int8 product alone: {dom_ms * 1e3:.3f} us per launch (h {h0.rows}x{h0.cols})")
         dom_desc = {"int8_ops_per_launch": step_flops, "us_per_launch": round(dom_ms * 1e3, 3),
@@ -560,42 +512,43 @@ def main():
         dom_desc = {"algorithmic_bytes_per_launch": step_bytes if kind != "gemm" else None,
                     "flops_per_launch": step_flops if kind == "gemm" else None,
                     "us_per_launch": round(ms_step * 1e3, 3)}
-    kname, ksrc = DOMINANT_KERNEL[args.workload]
-    traffic = traffic_from_profiles(args.workload, ksrc)
+    kname, ksrc = DOMINANT_KERNEL[name]
+    traffic = traffic_from_profiles(name, ksrc)
     roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
             "frac": round(achieved / peak, 4), "traffic": traffic,
             "kernel": kname, "launch": dom_desc,
             "launches_per_step": launches_per_step,
             "algorithmic_bytes_per_step": step_bytes, "flops_per_step": step_flops}
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_budget > 0:
         log("timing the oracle on the host cores")
-        cpu = cpu_baseline(kind, config, mats, batch, args.cpu_budget)
+        cpu = cpu_baseline(kind, config, mats, batch, cpu_budget)
     for hs in handles:
         for h in hs:
             Q.qmv_destroy(h)
-    wl = {"workload": args.workload, "description": desc, "batch": batch,
+    del handles
+    wl = {"workload": name, "description": desc, "config": config, "batch": batch,
           "matrices": [{"wtype": "Q8_0" if wt == Q8 else "Q4_0",
                         "scales": "f16" if sf else "f32", "rows": r, "cols": c}
                        for _, wt, sf, r, c in mats],
           "weight_copies_rotated": ncopies, "hip_graph": use_graph}
-    print(json.dumps({
+    return {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic (seeded; uniform quants and scales, N(0,1) "
                                 "activations)",
-        "config": wl, "roofline": roof, "cpu_baseline": cpu}), flush=True)
+        "config": wl, "roofline": roof, "cpu_baseline": cpu}
 
 
-def run_writer(args, desc, config, mats, stream):
+def run_writer(args, name, desc, config, mats, stream, cpu_budget):
     """The weight writer as a step: one qmv_quantize_weights call over a
     float32 matrix (rotated copies, >= 512 MB), captured in a graph."""
     import torch
     from block_quant_weight_amd import qmv as Q
     m, wt, sf, r, c = mats[0]
     step_bytes, _ = step_work("writer", mats, 1)
-    search = "search" in args.workload
+    search = "search" in name
     rule = Q.QMV_Q4_SEARCH if search else Q.QMV_Q4_ROUND
     w = torch.from_numpy(writer_weights(config, m, r, c)).cuda()
     ncopies = max(2, -(-ROTATE_BYTES // (4 * r * c)))
@@ -605,34 +558,19 @@ def run_writer(args, desc, config, mats, stream):
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     steps = args.steps if args.steps is not None else 200
     warmup = args.warmup if args.warmup is not None else 20
-    log(f"workload {args.workload}: {desc}; {ncopies} input copies; "
+    log(f"workload {name}: {desc}; {ncopies} input copies; "
         f"{steps} steps after {warmup} warm-up")
-    for i in range(warmup):
-        Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
+    Q.qmv_quantize_weights(wt, sf, ws[0], image, status=status, rule=rule)
     torch.cuda.synchronize()
     if int(status[0].item()) != 0:
         raise RuntimeError("writer reported an unstorable scale")
+
+    def step(i):
+        Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
     use_graph = not args.no_graph
-    if use_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(steps):
-                Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
-        g.replay()
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    if use_graph:
-        g.replay()
-    else:
-        for i in range(steps):
-            Q.qmv_quantize_weights(wt, sf, ws[i % ncopies], image, status=status, rule=rule)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
+    ms_step = timed_steps(step, steps, warmup, stream, use_graph, args.warm_seconds)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    kname, ksrc = DOMINANT_KERNEL[args.workload]
+    kname, ksrc = DOMINANT_KERNEL[name]
     launch = {"algorithmic_bytes_per_launch": step_bytes, "us_per_launch": round(ms_step * 1e3, 3)}
     if search:
         # bound by float32 arithmetic, not by memory
@@ -641,30 +579,192 @@ def run_writer(args, desc, config, mats, stream):
         launch["f32_ops_per_launch"] = ops
         roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(F32_OPS_PEAK_T, 3),
                 "unit": "Tops/s (float32, unfused)", "frac": round(achieved / F32_OPS_PEAK_T, 4),
-                "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
+                "traffic": traffic_from_profiles(name, ksrc), "kernel": kname,
                 "launch": launch, "launches_per_step": 1,
                 "algorithmic_bytes_per_step": step_bytes, "flops_per_step": ops}
     else:
         roof = {"bound": "hbm", "achieved": round(value, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(value / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profiles(args.workload, ksrc), "kernel": kname,
+                "traffic": traffic_from_profiles(name, ksrc), "kernel": kname,
                 "launch": launch, "launches_per_step": 1,
                 "algorithmic_bytes_per_step": step_bytes, "flops_per_step": None}
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_budget > 0:
         log("timing the oracle on the host cores")
-        cpu = cpu_baseline("writer_search" if search else "writer", config, mats, 1,
-                           args.cpu_budget)
-    wl = {"workload": args.workload, "description": desc, "batch": 1,
+        cpu = cpu_baseline("writer_search" if search else "writer", config, mats, 1, cpu_budget)
+    wl = {"workload": name, "description": desc, "config": config, "batch": 1,
           "matrices": [{"wtype": "Q8_0" if wt == Q8 else "Q4_0", "scales": "f16" if sf else "f32",
                         "rows": r, "cols": c}],
           "input_copies_rotated": ncopies, "hip_graph": use_graph}
-    print(json.dumps({
+    return {
         "metric": METRIC, "value": round(value, 3), "unit": "GB/s", "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; N(0,1) float32 weights)", "config": wl,
-        "roofline": roof, "cpu_baseline": cpu}), flush=True)
+        "roofline": roof, "cpu_baseline": cpu}
+
+
+def timed_steps(step, steps, warmup, stream, use_graph, warm_seconds):
+    """ms per step of step(i) for i in [warmup, warmup + steps): warmup
+    eager calls, then (use_graph) one captured graph of the timed steps,
+    replayed untimed for at least warm_seconds and then once under HIP events
+    on the launching stream (without a graph: the steps themselves, repeated
+    for the warm-up time, then once timed)."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                step(warmup + i)
+        run = g.replay
+    else:
+        def run():
+            for i in range(steps):
+                step(warmup + i)
+    t0 = time.perf_counter()
+    while True:
+        run()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_seconds:
+            break
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+# Read-ceiling sizes: the algorithmic bytes of each GEMV configuration's
+# largest launch, plus a spread of sizes around them.
+READ_SIZES = [1 << 18, 1 << 20, 1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26, 1 << 27, 1 << 28]
+
+
+def read_ceiling(nbytes, stream, args, steps=None):
+    """GB/s of qmv_read_probe over nbytes, each launch on a different part of
+    a buffer of >= 512 MB (every read from HBM), timed like a workload."""
+    import torch
+    from block_quant_weight_amd import qmv as Q
+    n = (nbytes + 255) // 256 * 256
+    copies = max(2, -(-ROTATE_BYTES // n))
+    buf = torch.empty(copies * n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    nb = nbytes // 16 * 16
+    if steps is None:
+        steps = 1000 if nbytes < (64 << 20) else 100
+
+    def step(i):
+        k = i % copies
+        Q.qmv_read_probe(buf[k * n:(k + 1) * n], nb, sink)
+    ms = timed_steps(step, steps, 5, stream, not args.no_graph, min(args.warm_seconds, 0.2))
+    del buf
+    return {"bytes": nb, "us_per_read": round(ms * 1e3, 3), "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies_rotated": copies}
+
+
+def read_stream(args, stream):
+    """The read ceiling over READ_SIZES and the GEMV configurations' launch sizes."""
+    sizes = sorted(set(READ_SIZES + [b for b in GEMV_LAUNCH_BYTES.values()]))
+    res = [read_ceiling(b, stream, args) for b in sizes]
+    for r in res:
+        log(f"read ceiling {r['bytes']:>11,d} B: {r['us_per_read']:9.3f} us, {r['GB/s']:7.1f} GB/s")
+    best = max(res, key=lambda r: r["GB/s"])
+    return {"metric": "read ceiling GB/s (qmv_read_probe)", "value": best["GB/s"], "unit": "GB/s",
+            "n_gpus": 1, "higher_is_better": True, "config": {"workload": "read_stream"},
+            "ceilings": res}
+
+
+def gemv_launch_bytes(name):
+    """Algorithmic bytes of each launch of a GEMV workload's step."""
+    desc, kind, config, mats, batch = workload(name)
+    groups = launch_groups(name, mats)
+    gated = name == "decode_layer_gated"
+    return [step_work(kind, [mats[j] for j in gr], batch, [list(range(len(gr)))], gated)[0]
+            for gr in groups]
+
+
+GEMV_WORKLOADS = ("q8_gemv_512", "q4_gemv_4096", "decode_layer", "lm_head_b1", "lm_head_b64")
+GEMV_LAUNCH_BYTES = {}
+for _n in GEMV_WORKLOADS:
+    for _k, _b in enumerate(gemv_launch_bytes(_n)):
+        GEMV_LAUNCH_BYTES[(_n, _k)] = _b
+
+# the default run: every configuration, headline first in importance
+ALL = ["q8_gemv_512", "q4_gemv_4096", "decode_layer", "gemm_q4_14336x4096",
+       "gemm_q8_4096x14336", "lm_head_b1", "lm_head_b64", "embed_64"]
+HEADLINE = "lm_head_b1"
+
+
+def with_ceiling(rec, name, args, stream):
+    """Adds the read ceiling at each launch's byte count to a GEMV record."""
+    roof = rec["roofline"]
+    launches = roof["launch"].get("every_launch") or [dict(roof["launch"], **{"GB/s": roof["achieved"]})]
+    out = []
+    for k, ln in enumerate(launches):
+        c = read_ceiling(GEMV_LAUNCH_BYTES[(name, k)], stream, args)
+        out.append({"matrices": ln.get("matrices", [0]), "bytes": c["bytes"],
+                    "launch_GB/s": ln["GB/s"], "ceiling_GB/s": c["GB/s"],
+                    "ceiling_us": c["us_per_read"],
+                    "frac_of_ceiling": round(ln["GB/s"] / c["GB/s"], 4)})
+        log(f"{name} launch {k}: {ln['GB/s']:.1f} GB/s against a read ceiling of "
+            f"{c['GB/s']:.1f} GB/s at {c['bytes']:,d} B")
+    roof["read_ceiling"] = out
+
+
+def summary(rec):
+    wl = rec["config"]
+    return {"config": wl.get("config"), "description": wl.get("description"),
+            "value": rec["value"], "unit": rec["unit"], "ms_per_step": rec["ms_per_step"],
+            "steps": rec["steps"], "roofline": rec["roofline"],
+            "cpu_baseline": rec["cpu_baseline"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="all")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=None,
+                    help="seconds of oracle time per workload (default 10 for one "
+                         "workload, 3 each for the default run)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="untimed replays of the step graph before timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(the product runs on a single MI355X; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    # One side stream for warm-up, capture and timing: the library keeps its
+    # split-K workspace per stream, so the capture stream must be warmed up.
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+
+    if args.workload != "all":
+        budget = 0.0 if args.no_cpu_baseline else (args.cpu_budget or 10.0)
+        rec = measure(args.workload, args, stream, budget)
+        print(json.dumps(rec), flush=True)
+        return
+    budget = 0.0 if args.no_cpu_baseline else (args.cpu_budget or 3.0)
+    recs = {}
+    for name in ALL:
+        log(f"=== {name}")
+        recs[name] = measure(name, args, stream, budget)
+        if name in GEMV_WORKLOADS:
+            with_ceiling(recs[name], name, args, stream)
+        torch.cuda.empty_cache()
+    head = dict(recs[HEADLINE])
+    head["configs"] = {name: summary(r) for name, r in recs.items()}
+    print(json.dumps(head), flush=True)
 
 
 if __name__ == "__main__":

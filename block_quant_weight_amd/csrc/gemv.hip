@@ -260,6 +260,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // the exact starting value -8 * sum_j Dk_j of each Tk.  Zero weights give
 // exactly zero; a non-finite activation makes its block's scale NaN.
 //
+// Small activations.  A nonzero value with |X| < 2^9 would keep fewer than
+// 10 significant bits, so it is not put in the digits (X = 0 there); a
+// 32-bit mask per chunk marks it, and after the chunk's digit sums each row
+// adds d * (v_j * x_j) in float32 for every marked j, in ascending order,
+// with x_j the activation itself.  Every other value keeps |X| >= 2^9, a
+// relative error of at most 2^-10, so each output is within about 2^-10 of
+// sum |w| |x| whatever the spread of a block's values.  For N(0,1) data
+// about 0.04% of the values are small.
+//
 // Work split: one wavefront owns NR consecutive rows; lane l reads the 16-byte
 // chunks l, l + 64, ... of each row (a Q4_0 chunk is a whole block, a Q8_0
 // chunk half a block).  Order of requests at entry:
@@ -274,7 +283,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 //   digit piece p (16 bytes = 16 digits of one plane) at ((k*P + p)*64 + l),
 //     Q4_0: P = 6, piece 2*plane + half; Q8_0: P = 3, piece = plane;
 //   then the block info at (k*64 + l): Q4_0 {-8*sum D0, -8*sum D1, -8*sum D2,
-//   2^(E-22)} as 16 bytes, Q8_0 2^(E-22) as 4 bytes.
+//   2^(E-22)} as 16 bytes, Q8_0 2^(E-22) as 4 bytes; then the small-value
+//   mask (4 bytes) and two float slots (8 bytes, the streaming kernel's copy
+//   of the first small values) per chunk.
 // A wave reading step k touches 64 consecutive 16-byte slots.
 // ---------------------------------------------------------------------------
 
@@ -301,10 +312,14 @@ struct DigitLayout {
     static constexpr int CW = (WT == kQ4) ? 32 : 16;   // weights per 16-byte chunk
     static constexpr int P = (WT == kQ4) ? 6 : 3;      // digit pieces per chunk
     static constexpr int INFO = (WT == kQ4) ? 16 : 4;  // info bytes per chunk
-    // bytes of one staged activation vector with S steps of 64 chunks
+    // bytes of one staged activation vector with S steps of 64 chunks:
+    // digit pieces, block info, a 32-bit mask of small elements and two
+    // float slots for small values per chunk
     static __host__ __device__ uint32_t vector_bytes(uint32_t S) {
-        return S * 64 * (P * 16 + INFO);
+        return S * 64 * (P * 16 + INFO + 4 + 8);
     }
+    static __host__ __device__ uint32_t mask_offset(uint32_t S) { return S * 64 * (P * 16 + INFO); }
+    static __host__ __device__ uint32_t slot_offset(uint32_t S) { return S * 64 * (P * 16 + INFO + 4); }
 };
 
 __device__ __forceinline__ int dpp_swap_pair_i(int v) {
@@ -330,40 +345,45 @@ __device__ __forceinline__ void transpose3(uint32_t w0, uint32_t w1, uint32_t w2
 // halves of a block sit in adjacent lanes of one wave, which exchange their
 // largest magnitude and digit sums.  `dig` and `info` point at the vector's
 // LDS area; h is the half block's index within its vector.
-template <uint32_t WT>
-__device__ __forceinline__ void stage_half(const float4 (&xv)[4], uint32_t h,
-                                           int4* __restrict__ dig, void* __restrict__ info) {
+template <uint32_t WT, bool SLOTS>
+__device__ __forceinline__ bool stage_half(const float4 (&xv)[4], uint32_t h,
+                                           int4* __restrict__ dig, void* __restrict__ info,
+                                           uint32_t* __restrict__ masks, float2* __restrict__ slots) {
     using L = DigitLayout<WT>;
     const float v[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
                          xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
     // largest magnitude as an integer maximum of the absolute bit patterns,
     // so that inf and NaN win over every finite value
-    // and the smallest nonzero magnitude (zeros count as the largest pattern)
-    uint32_t m = 0, mn = 0xFFFFFFFFu;
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t b = __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu;
-        m = max(m, b);
-        mn = min(mn, b - 1u);  // 0 wraps to the largest pattern
-    }
+    for (int i = 0; i < 16; ++i) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
     m = max(m, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(m))));
-    mn = min(mn, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(mn))));
     const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
-    // A block holding a nonzero value below 2^(E-12) would keep that value
-    // to worse than 2^-11 of itself in 24-bit fixed point: such a ("wide")
-    // block is marked by a negative factor and multiplied in float32 from the
-    // activations themselves (mn + 1 is the smallest nonzero magnitude).
-    const bool wide = mn != 0xFFFFFFFFu &&
-                      __builtin_bit_cast(float, mn + 1u) < __builtin_amdgcn_ldexpf(1.0f, E - 12);
     const float sx = m >= 0x7F800000u ? __builtin_bit_cast(float, 0x7FC00000u)
-                                      : __builtin_amdgcn_ldexpf(wide ? -1.0f : 1.0f, E - 22);
+                                      : __builtin_amdgcn_ldexpf(1.0f, E - 22);
     // X + 0x808080 in the low three bytes: rne(x * 2^(22-E)) by adding
-    // 1.5 * 2^23, whose bits are then 0x4B400000 + X
+    // 1.5 * 2^23, whose bits are then 0x4B400000 + X.  A nonzero value whose
+    // X is below 2^9 in magnitude would keep less than 10 significant bits:
+    // such a ("small") value is left out of the digits (X = 0 there), marked
+    // in the chunk's mask, and its product added in float32 from the
+    // activation itself after the digit sums.
+    // With SLOTS, the first two small values of the half block are kept as
+    // floats too.
     uint32_t u[16];
+    uint32_t small = 0;
+    float f0 = 0.f, f1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float t = __builtin_amdgcn_ldexpf(v[i], 22 - E) + 12582912.0f;
-        u[i] = __builtin_bit_cast(uint32_t, t) - 0x4ABF7F80u;
+        const uint32_t ui = __builtin_bit_cast(uint32_t, t) - 0x4ABF7F80u;
+        const bool sm = (ui - (0x808080u - 511u)) < 1023u &&
+                        (__builtin_bit_cast(uint32_t, v[i]) << 1) != 0u;
+        if constexpr (SLOTS) {
+            f1 = sm && small != 0 && (small & (small - 1)) == 0 ? v[i] : f1;
+            f0 = sm && small == 0 ? v[i] : f0;
+        }
+        small |= sm ? (1u << i) : 0u;
+        u[i] = sm ? 0x808080u : ui;
     }
     uint32_t pl[3][4];
 #pragma unroll
@@ -387,53 +407,81 @@ __device__ __forceinline__ void stage_half(const float4 (&xv)[4], uint32_t h,
             for (int g = 0; g < 4; ++g) a = __builtin_amdgcn_sdot4(pl[dd][g], 0x01010101, a, false);
             s[dd] = a + dpp_swap_pair_i(a);
         }
-        if (half == 0)
+        // the block's mask: element 16 * half + i of the block is bit
+        // 16 * half + i
+        const uint32_t mine = small << (16 * half);
+        const uint32_t both = mine | static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(mine)));
+        // slot h of the block: the half block's first small value
+        const float other = __builtin_bit_cast(float, dpp_swap_pair_i(__builtin_bit_cast(int, f0)));
+        if (half == 0) {
             static_cast<int4*>(info)[k * 64 + l] =
                 make_int4(-8 * s[0], -8 * s[1], -8 * s[2], __builtin_bit_cast(int, sx));
+            masks[k * 64 + l] = both;
+            if constexpr (SLOTS) slots[k * 64 + l] = make_float2(f0, other);
+        }
     } else {
         const uint32_t c = h, k = c >> 6, l = c & 63;
 #pragma unroll
         for (int dd = 0; dd < 3; ++dd)
             dig[(k * L::P + dd) * 64 + l] = make_int4(pl[dd][0], pl[dd][1], pl[dd][2], pl[dd][3]);
         static_cast<float*>(info)[k * 64 + l] = sx;
+        masks[k * 64 + l] = small;
+        if constexpr (SLOTS) slots[k * 64 + l] = make_float2(f0, f1);
     }
+    return small != 0;
 }
 
-// Float32 sums of one chunk for a wide block: sum_j v_j x_j with the codes
-// v_j as they are (Q4_0: nibble - 8, element j from the low nibble of byte j
-// and element j + 16 from its high nibble; Q8_0: the signed quant), the
-// activations xc[0 .. CW) read again from memory.
-__device__ __forceinline__ float q4_f32_dot(const uint4 w, const float* __restrict__ xc) {
-    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-    const float4* x4 = reinterpret_cast<const float4*>(xc);
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 lo = x4[i], hi = x4[4 + i];
-        const float xl[4] = {lo.x, lo.y, lo.z, lo.w}, xh[4] = {hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int b = static_cast<int>((q[i] >> (8 * k)) & 0xFFu);
-            acc = fmaf(static_cast<float>((b & 15) - 8), xl[k], acc);
-            acc = fmaf(static_cast<float>((b >> 4) - 8), xh[k], acc);
+// Code of element j of a 16-byte chunk as a float: Q4_0 nibble - 8 (element
+// j from byte j % 16, low nibble for j < 16), Q8_0 the signed byte j.
+template <uint32_t WT>
+__device__ __forceinline__ float chunk_code(const uint4 q, uint32_t j) {
+    const uint32_t byte = WT == kQ4 ? (j & 15u) : j;
+    const uint32_t wi = byte >> 2;
+    const uint32_t w = wi == 0 ? q.x : wi == 1 ? q.y : wi == 2 ? q.z : q.w;
+    const uint32_t sh = 8 * (byte & 3u) + (WT == kQ4 ? 4 * (j >> 4) : 0);
+    if constexpr (WT == kQ4) return static_cast<float>(static_cast<int>((w >> sh) & 15u) - 8);
+    else return static_cast<float>(static_cast<int8_t>((w >> sh) & 0xFFu));
+}
+
+// Adds the small activations of one chunk (mask bits, left out of the digit
+// sums) of every row: acc[r] += d[r] * (v[r][j] * x_j), in ascending j.  x_j
+// comes from the chunk's two float slots if SLOTS (Q4_0: the first small
+// value of each half block; Q8_0: the first two), or else from xc in memory.
+template <uint32_t WT, bool SF16, bool SLOTS, int NR, int SMAX>
+__device__ __forceinline__ void small_rows(const uint4 (&qv)[NR][SMAX], const uint32_t (&dv)[NR][SMAX],
+                                           int k, uint32_t mask, const float2* __restrict__ slot,
+                                           const float* __restrict__ xc, float (&acc)[NR]) {
+    if (mask == 0) return;
+    const float2 sv = SLOTS ? *slot : make_float2(0.f, 0.f);
+    uint32_t used = 0;  // slots taken
+    while (mask != 0) {
+        const uint32_t j = __builtin_ctz(mask);
+        mask &= mask - 1;
+        // the slot this value may sit in
+        const uint32_t want = WT == kQ4 ? 1u + (j >> 4) : (used == 0 ? 1u : 2u);
+        float xj;
+        if (SLOTS && (used & want) == 0 && (WT == kQ4 || used != 3u)) {
+            xj = want == 1u ? sv.x : sv.y;
+            used |= want;
+        } else {
+            xj = xc[j];
         }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+            acc[r] = fmaf(scale_from_bits<SF16>(dv[r][k]), chunk_code<WT>(qv[r][k], j) * xj, acc[r]);
     }
-    return acc;
 }
 
-__device__ __forceinline__ float q8_f32_dot(const uint4 w, const float* __restrict__ xc) {
-    const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-    const float4* x4 = reinterpret_cast<const float4*>(xc);
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 xv = x4[i];
-        const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            acc = fmaf(static_cast<float>(static_cast<int8_t>((q[i] >> (8 * k)) & 0xFFu)), xs[k], acc);
-    }
-    return acc;
+// Workgroup-uniform OR of each thread's `mine` (every wave writes its own
+// slot of `slots`, read after the barrier that this call performs).
+__device__ __forceinline__ bool barrier_any(bool mine, uint32_t* slots, uint32_t waves) {
+    const uint32_t wid = threadIdx.x >> 6;
+    const bool w = __ballot(mine) != 0;
+    if ((threadIdx.x & 63) == 0) slots[wid] = w ? 1u : 0u;
+    __syncthreads();
+    uint32_t any = 0;
+    for (uint32_t i = 0; i < waves; ++i) any |= slots[i];
+    return any != 0;
 }
 
 // T0 + 256 T1 + 65536 T2 in float32 (T1 + 256 T2 is exact in int32).
@@ -479,15 +527,13 @@ __device__ __forceinline__ float q8_digit_dot(const uint4 w, const int4 (&pc)[3]
 
 // Adds one chunk of every row (quants qv[r][k], scale bits dv[r][k]) times
 // the staged activations of one vector (digit pieces pc, block info at
-// slot `is` of `info`) to acc[r], where `valid`.  A wide block (negative
-// factor) is multiplied in float32 from xc, its activations in memory.
+// slot `is` of `info`) to acc[r], where `valid`.
 template <uint32_t WT, bool SF16, int NR, int SMAX>
 __device__ __forceinline__ void chunk_rows(const uint4 (&qv)[NR][SMAX], const uint32_t (&dv)[NR][SMAX],
                                            int k, const int4 (&pc)[DigitLayout<WT>::P],
-                                           const uint8_t* __restrict__ info, uint32_t is,
-                                           const float* __restrict__ xc, bool valid,
+                                           const uint8_t* __restrict__ info, uint32_t is, bool valid,
                                            float (&acc)[NR]) {
-    float t[NR], f[NR];
+    float t[NR];
     float sx;
     if constexpr (WT == kQ4) {
         const int4 in = reinterpret_cast<const int4*>(info)[is];
@@ -500,18 +546,8 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&qv)[NR][SMAX], const ui
         for (int r = 0; r < NR; ++r) t[r] = q8_digit_dot(qv[r][k], pc);
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r) f[r] = scale_from_bits<SF16>(dv[r][k]) * sx;
-    // (only for chunks inside the row: past its end the slot is never written)
-    if (__builtin_expect(valid && sx < 0.f, 0)) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            t[r] = WT == kQ4 ? q4_f32_dot(qv[r][k], xc) : q8_f32_dot(qv[r][k], xc);
-            f[r] = scale_from_bits<SF16>(dv[r][k]);
-        }
-    }
-#pragma unroll
     for (int r = 0; r < NR; ++r) {
-        const float a = fmaf(f[r], t[r], acc[r]);
+        const float a = fmaf(scale_from_bits<SF16>(dv[r][k]) * sx, t[r], acc[r]);
         acc[r] = valid ? a : acc[r];
     }
 }
@@ -600,10 +636,15 @@ __device__ __forceinline__ void oneshot_body(
     }
 
     // ---- 3. activations -> digits in LDS ----
+    const uint32_t mask_off = L::mask_offset(S);
+    constexpr bool SLOTS_ = false;  // small values read from memory
+    bool mysmall = false;
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t b = j / nhalf, h = j - b * nhalf;
         uint8_t* base = lds + b * vec_bytes;
-        stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
+        mysmall |= stage_half<WT, SLOTS_>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes,
+                                  reinterpret_cast<uint32_t*>(base + mask_off),
+                                  reinterpret_cast<float2*>(base + L::slot_offset(S)));
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -616,7 +657,8 @@ __device__ __forceinline__ void oneshot_body(
         for (int g = 0; g < 4; ++g) xv[g] = x4[4ull * j + g];
         stage(j, xv);
     }
-    __syncthreads();
+    __shared__ uint32_t small_slots[WAVES];
+    const bool any_small = barrier_any(mysmall, small_slots, WAVES);
     if (wrows == 0) return;  // uniform per wave, after the barrier
 
     // ---- 4. multiply ----
@@ -636,9 +678,18 @@ __device__ __forceinline__ void oneshot_body(
                 int4 pc[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
-                const float* xc = x + static_cast<uint64_t>(b) * cols + (lane + 64u * k) * CW;
-                chunk_rows<WT, SF16, NR>(qv, dv, k, pc, base + dig_bytes, k * 64 + lane, xc, valid,
+                chunk_rows<WT, SF16, NR>(qv, dv, k, pc, base + dig_bytes, k * 64 + lane, valid,
                                          acc[b]);
+                // then the chunk's small activations, left out of the digits
+                // (a workgroup without any skips this)
+                if (any_small) {
+                    const uint32_t* mk = reinterpret_cast<const uint32_t*>(base + mask_off);
+                    const uint32_t mask = valid ? mk[k * 64 + lane] : 0u;
+                    small_rows<WT, SF16, false, NR>(
+                        qv, dv, k, mask,
+                        reinterpret_cast<const float2*>(base + L::slot_offset(S)) + k * 64 + lane,
+                        x + static_cast<uint64_t>(b) * cols + (lane + 64u * k) * CW, acc[b]);
+                }
             }
         }
     }
@@ -810,7 +861,7 @@ __device__ __forceinline__ float ffn_act(float a, uint32_t act) {
 
 // Multiplies a loaded tile by the NB staged vectors and stores its rows.
 // Gated (GATED = true): stores act(w1 row) * (w3 row) for each row pair.
-template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED>
+template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED, bool SMALL>
 __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<NR, SMAX>& b,
                                              const uint8_t* __restrict__ lds,
                                              const float* __restrict__ x, uint32_t cols,
@@ -836,9 +887,19 @@ __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<N
                 int4 pc[P];
 #pragma unroll
                 for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
-                const float* xc = x + static_cast<uint64_t>(v) * cols + (lane + 64u * k) * L::CW;
-                chunk_rows<WT, SF16, NR>(b.q, b.d, k, pc, base + dig_bytes, k * 64 + lane, xc, valid,
+                chunk_rows<WT, SF16, NR>(b.q, b.d, k, pc, base + dig_bytes, k * 64 + lane, valid,
                                          acc[v]);
+                // then the chunk's small activations (the one-shot kernel's
+                // order, so that both give the same sums)
+                if constexpr (SMALL) {
+                    const uint32_t* mk =
+                        reinterpret_cast<const uint32_t*>(base + L::mask_offset(S));
+                    const uint32_t mask = valid ? mk[k * 64 + lane] : 0u;
+                    small_rows<WT, SF16, true, NR>(
+                        b.q, b.d, k, mask,
+                        reinterpret_cast<const float2*>(base + L::slot_offset(S)) + k * 64 + lane,
+                        x + static_cast<uint64_t>(v) * cols + (lane + 64u * k) * L::CW, acc[v]);
+                }
             }
         }
     }
@@ -919,10 +980,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     };
     load_any(tile(t), ra);
 
+    const uint32_t mask_off = L::mask_offset(S);
+    constexpr bool SLOTS_ = true;  // small values kept in LDS
+    bool mysmall = false;
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t v = j / nhalf, h = j - v * nhalf;
         uint8_t* base = lds + v * vec_bytes;
-        stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
+        mysmall |= stage_half<WT, SLOTS_>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes,
+                                  reinterpret_cast<uint32_t*>(base + mask_off),
+                                  reinterpret_cast<float2*>(base + L::slot_offset(S)));
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -935,18 +1001,25 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
         for (int c = 0; c < 4; ++c) xv[c] = x4[4ull * j + c];
         stage(j, xv);
     }
-    __syncthreads();
+    __shared__ uint32_t small_slots[kStreamWaves];
+    const bool any_small = barrier_any(mysmall, small_slots, kStreamWaves);
 
-    // two register sets: the next tile's loads are in flight
-    while (t < end) {
-        load_any(tile(t + step), rb);
-        compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, ra, lds, x, cols, S, lane, act);
-        t += step;
-        if (t >= end) break;
-        load_any(tile(t + step), ra);
-        compute_tile<WT, SF16, NR, NB, SMAX, GATED>(g, rb, lds, x, cols, S, lane, act);
-        t += step;
-    }
+    // two register sets: the next tile's loads are in flight (the loop
+    // without the small-activation pass unless a staged value is small)
+    auto run = [&](auto small_t) {
+        constexpr bool W = decltype(small_t)::value;
+        while (t < end) {
+            load_any(tile(t + step), rb);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, ra, lds, x, cols, S, lane, act);
+            t += step;
+            if (t >= end) break;
+            load_any(tile(t + step), ra);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, rb, lds, x, cols, S, lane, act);
+            t += step;
+        }
+    };
+    if (any_small) run(std::true_type{});
+    else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------

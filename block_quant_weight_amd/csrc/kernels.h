@@ -94,4 +94,7 @@ hipError_t launch_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,
 hipError_t launch_block_dots(const MatView& m, const int8_t* xq, int32_t* s,
                              hipStream_t stream);
 
+// Reads n16 16-byte words from src (measurement aid: the read ceiling).
+hipError_t launch_read_probe(const void* src, uint64_t n16, uint32_t* sink, hipStream_t stream);
+
 }  // namespace qmv

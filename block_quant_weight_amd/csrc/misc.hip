@@ -7,6 +7,12 @@
 // and "Q4_0" give v and w = v * d).  One wavefront per id; lane l decodes
 // the 16-byte quant chunks l, l + 64, ... of the row.
 //
+// Read probe (a measurement aid, no part of the product): each workgroup
+// reads its own 32 KiB with 1 KiB-per-wave loads, all requested at once; the
+// words are folded by XOR and stored only in the (practically never met)
+// case that the fold equals a fixed constant, which keeps the loads without
+// a store stream.
+//
 // Quantizer: the page's "Quantization rule" in separate float32 operations
 // (__fmul_rn / __fadd_rn cannot be fused; float division is correctly
 // rounded on this target).
@@ -159,6 +165,34 @@ __global__ __launch_bounds__(256) void block_dots_kernel(
     s[idx] = acc;
 }
 
+constexpr uint32_t kProbeMagic = 0x9E3779B9u;
+constexpr uint32_t kProbeLoads = 8;                          // 16-byte loads per thread
+constexpr uint32_t kProbeBytes = 256 * kProbeLoads * 16;     // bytes per workgroup
+
+// Workgroup g reads bytes [g * 32 KiB, (g + 1) * 32 KiB) of src: every load
+// requested before any is used (one round trip, like the one-shot product
+// kernels), raw buffer loads with the streaming cache policy of the weight
+// streams, zeros past the end.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint8_t* __restrict__ src, uint64_t nbytes,
+                                                         uint32_t* __restrict__ sink) {
+    const uint64_t base = static_cast<uint64_t>(blockIdx.x) * kProbeBytes;
+    const uint64_t left = nbytes - base;
+    const uint32_t range = left < kProbeBytes ? static_cast<uint32_t>(left) : kProbeBytes;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(src + base), static_cast<short>(0), static_cast<int>(range), 0x00020000);
+    uint32_t v[kProbeLoads][4];
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeLoads; ++u) {
+        typedef uint32_t probe_u32x4 __attribute__((ext_vector_type(4)));
+        const probe_u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, (u * 256 + threadIdx.x) * 16, 0, 2);
+        v[u][0] = t[0]; v[u][1] = t[1]; v[u][2] = t[2]; v[u][3] = t[3];
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (uint32_t u = 0; u < kProbeLoads; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    if (acc == kProbeMagic) sink[blockIdx.x & 63] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,
@@ -199,6 +233,15 @@ hipError_t launch_block_dots(const MatView& m, const int8_t* xq, int32_t* out,
     else
         hipLaunchKernelGGL((block_dots_kernel<kQ8>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
                            m.q, xq, out, m.rows, m.cols);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, uint64_t n16, uint32_t* sink, hipStream_t s) {
+    const uint64_t nbytes = n16 * 16;
+    const uint64_t grid = (nbytes + kProbeBytes - 1) / kProbeBytes;
+    if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(src), nbytes, sink);
     return hipGetLastError();
 }
 

@@ -365,4 +365,11 @@ int qmv_block_dots(qmv_handle h, const int8_t* xq, int32_t* s, void* stream) {
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int qmv_read_probe(const void* src, uint64_t nbytes, uint32_t* sink, void* stream) {
+    if (src == nullptr || sink == nullptr || nbytes == 0 || nbytes % 16 != 0) return QMV_E_ARG;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return QMV_E_ARG;
+    return device_status(qmv::launch_read_probe(src, nbytes / 16, sink,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -23,7 +23,8 @@ QMV_E_NOMEM = -5
 EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
-           "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated", "qmv_gemm_q8")
+           "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated", "qmv_gemm_q8",
+           "qmv_read_probe")
 
 _lib = None
 
@@ -40,6 +41,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} is not built: run `python -m block_quant_weight_amd.build`")
+        # torch first: its HIP runtime must be the one the library binds to
+        # (a second runtime loaded ahead of it would not know torch's streams
+        # or memory)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         u32, u64, i32, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p
         pu64 = ctypes.POINTER(u64)
@@ -61,6 +66,7 @@ def lib():
             "qmv_quantize_weights": ([u32, u32, u32, u32, u32, vp, vp, u64, vp, vp], i32),
             "qmv_gemv_gated": ([vp, vp, u32, vp, vp, u32, vp], i32),
             "qmv_gemm_q8": ([vp, vp, vp, vp, u32, vp], i32),
+            "qmv_read_probe": ([vp, u64, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -297,3 +303,15 @@ def qmv_block_dots(h: QmvHandle, xq, s, stream=None):
     px = _dev(xq, torch.int8, h.cols, "xq")
     ps = _dev(s, torch.int32, h.rows * (h.cols // 32), "s")
     _check(lib().qmv_block_dots(h.ptr, px, ps, _stream(stream)), "qmv_block_dots")
+
+
+def qmv_read_probe(src, nbytes, sink, stream=None):
+    """Reads nbytes of the GPU tensor src (from its start; a measurement
+    aid); sink: int32 or uint32 GPU tensor of at least 64 elements."""
+    import torch
+    if not (src.is_cuda and sink.is_cuda) or sink.numel() < 64 or sink.element_size() != 4:
+        raise QmvError(QMV_E_ARG, "qmv_read_probe")
+    if nbytes > src.numel() * src.element_size():
+        raise QmvError(QMV_E_ARG, "qmv_read_probe")
+    _check(lib().qmv_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)),
+           "qmv_read_probe")

@@ -162,10 +162,11 @@ int qmv_destroy(qmv_handle h);
  * of weight codes times activation digits are exact integer dot products
  * (the Q8_0 activation quantization of the .mlb page's "Quantization rule",
  * with three int8 digits instead of one), and blocks are accumulated in
- * float32.  A block holding a nonzero activation more than 2^12 below its
- * amax (which the fixed point would keep to worse than 2^-11 of itself) is
- * multiplied in float32 from the activations instead.  A non-finite
- * activation makes the outputs of its batch row NaN.
+ * float32.  A nonzero activation that the fixed point would keep to fewer
+ * than 10 significant bits (more than about 2^13 below its block's amax) is
+ * left out of the digits and its products are added in float32 from the
+ * activation itself, so every activation counts to within 2^-10 of itself.
+ * A non-finite activation makes the outputs of its batch row NaN.
  * Larger batches (an LM head over a batch of hidden states, say) run on the
  * matrix cores with f16 operands and float32 accumulation: each token's
  * activations scaled by a power of two from its largest magnitude and
@@ -337,6 +338,16 @@ int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule, uint
  * Errors: QMV_E_ARG (null or misaligned pointer, no upload), QMV_E_DEVICE.
  */
 int qmv_block_dots(qmv_handle h, const int8_t *xq, int32_t *s, void *stream);
+
+/*
+ * Measurement aid, not part of the product: reads nbytes of device memory
+ * at src with 16-byte loads (1 KiB per wavefront load, 32 KiB per
+ * workgroup, all requested at once), the read ceiling against which the
+ * decode kernels' rates are set.  src 16-byte aligned, nbytes a nonzero multiple of 16;
+ * sink: 64 uint32 of device memory the kernel may write (it keeps the loads
+ * alive; practically never written).  Errors: QMV_E_ARG, QMV_E_DEVICE.
+ */
+int qmv_read_probe(const void *src, uint64_t nbytes, uint32_t *sink, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *qmv_status_str(int status);
