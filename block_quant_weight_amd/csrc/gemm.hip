@@ -521,6 +521,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     const __amdgpu_buffer_rsrc_t orr =
         rsrc(out + (static_cast<uint64_t>(split) * M + m0) * N + n0, mrows * N * 4);
     const __amdgpu_buffer_rsrc_t er = rsrc(rexp + n0, nrows * 4);
+    // a tile's output fits one 32-bit buffer range unless rows are very
+    // many (2^22 or more): then plain stores with a bounds test
+    const bool ranged = N < (1u << 22);
+    float* const obase = out + (static_cast<uint64_t>(split) * M + m0) * N + n0;
     auto finish = [&](auto JK) {
         constexpr int jk = decltype(JK)::value;
         const int partner = (1 - kg) * C::WM + wm;
@@ -536,9 +540,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
                     const float sum = acc[i][jk + jj][v] + red[(((partner * 2 + jj) * 2 + i) * 16 + v) * 64 + lane];
                     const int t = ts[i][v >> 2][v & 3];
                     const uint32_t ml = mw + 32 * i + 8 * (v >> 2) + (v & 3);
-                    const uint32_t off = nl < nrows ? ml * N * 4 + ob : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_ldexpf(sum, -(rsh + t))), orr, off, 0, 0);
+                    const float val = __builtin_amdgcn_ldexpf(sum, -(rsh + t));
+                    if (ranged) {
+                        const uint32_t off = nl < nrows ? ml * N * 4 + ob : kOob;
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), orr, off, 0, 0);
+                    } else if (nl < nrows && ml < mrows) {
+                        obase[static_cast<uint64_t>(ml) * N + nl] = val;
+                    }
                 }
         }
     };
@@ -664,10 +672,8 @@ size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool /*x_f32*/) {
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y, uint32_t batch,
                        void* workspace, hipStream_t s) {
     if (workspace == nullptr) return hipErrorInvalidValue;
-    // the scale array is addressed through one 32-bit buffer range, and so
-    // is a tile's 256 tokens of output
-    if (uint64_t{m.rows} * (m.cols / 32) * (m.scale_f16 ? 2 : 4) >= 0xFFFFFFF0ull ||
-        uint64_t{m.rows} * 256 * 4 >= 0xFFFFFFF0ull)
+    // the scale array is addressed through one 32-bit buffer range
+    if (uint64_t{m.rows} * (m.cols / 32) * (m.scale_f16 ? 2 : 4) >= 0xFFFFFFF0ull)
         return hipErrorNotSupported;
     const Plan p0 = make_plan(m, batch);
     if (p0.pass == 0) return hipErrorInvalidValue;

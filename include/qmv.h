@@ -235,10 +235,8 @@ int qmv_gemv_gated(qmv_handle w1, qmv_handle w3, uint32_t act, const float *x,
  * holding inf or NaN gets NaN outputs.  When the matrix has too few tiles to
  * fill the GPU the K dimension is split and the slices' partial sums are
  * added in slice order by a third kernel (deterministic).  Errors: as
- * qmv_gemv, plus QMV_E_SHAPE for matrices of 2^22 rows or more (a tile's
- * output is addressed through one 32-bit range), QMV_E_ARG for a first call
- * on a stream under graph capture and QMV_E_NOMEM if its workspace cannot be
- * allocated.
+ * qmv_gemv, plus QMV_E_ARG for a first call on a stream under graph
+ * capture and QMV_E_NOMEM if its workspace cannot be allocated.
  */
 int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
              void *stream);
