@@ -62,6 +62,8 @@
 // in that XCD's L2.  When the tiles are too few for the compute units, K
 // is split and a second kernel adds the slices' partial sums in slice order
 // (deterministic).
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -709,6 +711,64 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y, ui
             if (e != hipSuccess) return e;
         }
         done += M;
+    }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for callers that cannot allocate (qmv_gemm_noalloc): one
+// array per GPU, held until the process ends.  Its address on a device is
+// found once, with that device current; host code uses only that address.
+// Every call on a GPU shares the array: calls that overlap on one GPU race.
+// Nothing in it needs clearing (the staging and product kernels write
+// every byte they read).
+// ---------------------------------------------------------------------------
+constexpr size_t kGemmScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) uint8_t scratch[kGemmScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t gemm_scratch(void** ptr, size_t* bytes) {
+    *ptr = nullptr;
+    *bytes = 0;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    *bytes = kGemmScratchBytes;
+    return hipSuccess;
+}
+
+hipError_t launch_gemm_within(const MatView& m, const void* x, bool x_f32, float* y,
+                              uint32_t batch, void* workspace, size_t ws_bytes, hipStream_t s) {
+    if (workspace == nullptr || batch == 0) return hipErrorInvalidValue;
+    // the largest pass (a multiple of 32 tokens, or the whole batch) whose
+    // workspace fits
+    uint32_t n = batch;
+    while (gemm_workspace_bytes(m, n, x_f32) > ws_bytes) {
+        if (n <= kTokensPerTile) return hipErrorNotSupported;
+        n = (n / 2 + kTokensPerTile - 1) / kTokensPerTile * kTokensPerTile;
+    }
+    const uint64_t xs = uint64_t{m.cols} * (x_f32 ? 4 : 2);
+    for (uint32_t done = 0; done < batch;) {
+        const uint32_t k = batch - done < n ? batch - done : n;
+        const hipError_t e = launch_gemm(m, static_cast<const uint8_t*>(x) + uint64_t{done} * xs, x_f32,
+                                         y + uint64_t{done} * m.rows, k, workspace, s);
+        if (e != hipSuccess) return e;
+        done += k;
     }
     return hipSuccess;
 }

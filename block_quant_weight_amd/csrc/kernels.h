@@ -48,6 +48,16 @@ size_t gemm_workspace_bytes(const MatView& m, uint32_t batch, bool x_f32);
 hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y,
                        uint32_t batch, void* workspace, hipStream_t stream);
 
+// The library's fixed GEMM scratch on the current device (its address, found
+// once per device, and its size).
+hipError_t gemm_scratch(void** ptr, size_t* bytes);
+// launch_gemm over a workspace of ws_bytes: the batch is taken in passes of
+// at most that workspace (hipErrorNotSupported if a pass of 32 tokens needs
+// more).
+hipError_t launch_gemm_within(const MatView& m, const void* x, bool x_f32, float* y,
+                              uint32_t batch, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
 // y[i] = sum over z < splits of part[z * total + i], added in z order.
 hipError_t launch_splitk_sum(const float* part, float* y, uint64_t total, uint32_t splits,
                              hipStream_t stream);

@@ -304,6 +304,22 @@ int qmv_gemm(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
     return device_status(e);
 }
 
+int qmv_gemm_noalloc(qmv_handle h, const uint16_t* x_bf16, float* y, uint32_t batch,
+                     void* stream) {
+    int st = ready(h);
+    if (st != QMV_OK) return st;
+    if (x_bf16 == nullptr || y == nullptr || batch == 0) return QMV_E_ARG;
+    if (!aligned16(x_bf16) || !aligned16(y)) return QMV_E_ARG;
+    void* ws = nullptr;
+    size_t wsb = 0;
+    hipError_t e = qmv::gemm_scratch(&ws, &wsb);
+    if (e != hipSuccess) return QMV_E_DEVICE;
+    e = qmv::launch_gemm_within(view(h), x_bf16, false, y, batch, ws, wsb,
+                                static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return QMV_E_SHAPE;
+    return device_status(e);
+}
+
 int qmv_gemm_q8(qmv_handle h, const int8_t* xq, const float* dx, float* y, uint32_t batch,
                 void* stream) {
     int st = ready(h);

@@ -24,7 +24,7 @@ EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
            "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated", "qmv_gemm_q8",
-           "qmv_read_probe")
+           "qmv_read_probe", "qmv_gemm_noalloc")
 
 _lib = None
 
@@ -67,6 +67,7 @@ def lib():
             "qmv_gemv_gated": ([vp, vp, u32, vp, vp, u32, vp], i32),
             "qmv_gemm_q8": ([vp, vp, vp, vp, u32, vp], i32),
             "qmv_read_probe": ([vp, u64, vp, vp], i32),
+            "qmv_gemm_noalloc": ([vp, vp, vp, u32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -276,6 +277,16 @@ def qmv_gemm(h: QmvHandle, x_bf16, y, batch=None, stream=None):
     px = _dev(x_bf16, torch.bfloat16, b * h.cols, "x_bf16")
     py = _dev(y, torch.float32, b * h.rows, "y")
     _check(lib().qmv_gemm(h.ptr, px, py, b, _stream(stream)), "qmv_gemm")
+
+
+def qmv_gemm_noalloc(h: QmvHandle, x_bf16, y, batch=None, stream=None):
+    """qmv_gemm on the library's fixed scratch (no allocation); calls that
+    overlap on one GPU race."""
+    import torch
+    b = batch if batch is not None else x_bf16.shape[0]
+    px = _dev(x_bf16, torch.bfloat16, b * h.cols, "x_bf16")
+    py = _dev(y, torch.float32, b * h.rows, "y")
+    _check(lib().qmv_gemm_noalloc(h.ptr, px, py, b, _stream(stream)), "qmv_gemm_noalloc")
 
 
 def qmv_embed_rows(h: QmvHandle, ids, out, stream=None):

@@ -242,6 +242,22 @@ int qmv_gemm(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
              void *stream);
 
 /*
+ * qmv_gemm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and results, with the staged activations and split-K
+ * partial sums in a fixed 64 MiB array of the library's own on each GPU
+ * (held until the process ends) instead of an allocated workspace.  No
+ * allocation happens in this call.  A batch whose workspace would exceed the
+ * array is taken in passes of fewer tokens (a multiple of 32); QMV_E_SHAPE
+ * if even a pass of 32 tokens does not fit (rows or cols very large).  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (different streams, or host threads) race and must be serialised by the
+ * caller.  Arguments and other errors as qmv_gemm.
+ */
+int qmv_gemm_noalloc(qmv_handle h, const uint16_t *x_bf16, float *y, uint32_t batch,
+                     void *stream);
+
+/*
  * Prefill product on Q8_0-quantized activations (the page's CPU path: the
  * activations quantized per block of 32 by the "Quantization rule", e.g.
  * with qmv_quantize_q8, then per-block integer dot products):
