@@ -35,6 +35,11 @@ int device_status(hipError_t e) {
     return QMV_E_DEVICE;
 }
 
+// The launchers check their launches with hipGetLastError, which also
+// returns an error left by any earlier failed runtime call of this thread
+// (a failed allocation, say); each call that launches clears it first.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 // Common checks of a compute call on an uploaded handle.  The call must run
 // on the device that holds the matrix.
 int ready(const qmv_mat* h) {
@@ -42,6 +47,7 @@ int ready(const qmv_mat* h) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return QMV_E_DEVICE;
     if (cur != h->device) return QMV_E_ARG;
+    clear_stale_error();
     return QMV_OK;
 }
 
@@ -173,6 +179,7 @@ int qmv_upload(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
 }
 
 int qmv_upload_gguf(qmv_handle h, const void* src, uint64_t nbytes, void* stream) {
+    clear_stale_error();
     if (h == nullptr || src == nullptr) return QMV_E_ARG;
     if (h->dev != nullptr) return QMV_E_ARG;  // uploaded once, then read-only
     const qmv::Layout& L = h->layout;
@@ -349,6 +356,7 @@ int qmv_embed_rows(qmv_handle h, const int32_t* ids, uint32_t n, float* out,
 int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule, uint32_t rows,
                          uint32_t cols, const float* w, void* image, uint64_t image_bytes,
                          uint32_t* status, void* stream) {
+    clear_stale_error();
     qmv::Layout L;
     int st = qmv::compute_layout(wtype, scale_f16, rows, cols, &L);
     if (st != QMV_OK) return st;
@@ -365,6 +373,7 @@ int qmv_quantize_weights(uint32_t wtype, uint32_t scale_f16, uint32_t rule, uint
 
 int qmv_quantize_q8(const float* x, uint64_t n, int8_t* q, float* d,
                     void* stream) {
+    clear_stale_error();
     if (x == nullptr || q == nullptr || d == nullptr || n == 0) return QMV_E_ARG;
     if (!aligned16(x) || !aligned16(q) || !aligned16(d)) return QMV_E_ARG;
     if (n % 32 != 0) return QMV_E_SHAPE;
@@ -382,6 +391,7 @@ int qmv_block_dots(qmv_handle h, const int8_t* xq, int32_t* s, void* stream) {
 }
 
 int qmv_read_probe(const void* src, uint64_t nbytes, uint32_t* sink, void* stream) {
+    clear_stale_error();
     if (src == nullptr || sink == nullptr || nbytes == 0 || nbytes % 16 != 0) return QMV_E_ARG;
     if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return QMV_E_ARG;
     return device_status(qmv::launch_read_probe(src, nbytes / 16, sink,

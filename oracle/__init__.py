@@ -21,6 +21,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libqmv_oracle.so")
+# a sanitizer build of the same source, loaded instead when set (the
+# sanitizer test runs the oracle's pins against it in a child process)
+_LIB_OVERRIDE = os.environ.get("QMV_ORACLE_LIB")
 
 Q8_0 = 1
 Q4_0 = 2
@@ -43,9 +46,12 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        L = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            L = ctypes.CDLL(_LIB_PATH)
         u32, u64, i32 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
         vp = ctypes.c_void_p
         L.orc_span.argtypes = [u32, u32, u64, u64, vp]
