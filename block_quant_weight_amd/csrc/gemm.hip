@@ -1,8 +1,9 @@
 // Prefill product (GEMM) on the gfx950 matrix cores, with f16 operands.
 //
 // Y[t][r] = sum_c W[r][c] * X[t][c] (Krafla ".mlb model, version 1" page,
-// "Body"; w = q * d for Q8_0, w = (nibble - 8) * d for Q4_0 with byte j of a
-// block holding element j low and j + 16 high, sections "Q8_0" and "Q4_0"),
+// "Body"; w = q * d for Q8_0, w = (nibble - 8) * d for Q4_0, where the
+// first 16 elements of a block take the low halves of its 16 bytes in order
+// and the last 16 the high halves, sections "Q8_0" and "Q4_0"),
 // t over the batch of activation rows.  This is the one place where the
 // product is a dense contraction, so it runs on v_mfma_f32_32x32x16_f16
 // (measured at 1.76 PFLOP/s back to back on this GPU, against 1.2 for the

@@ -16,8 +16,8 @@
 // of at most 64) x 128 weight rows and walks its slice of K in steps of two
 // blocks; when the tiles alone leave compute units idle, K is split into
 // slices whose partial sums a second kernel adds in slice order.  Each step's activation quants, weight
-// codes (Q4_0 nibbles turned into signed bytes n - 8 on the way: byte j of
-// a block gives element j from its low nibble and j + 16 from its high one)
+// codes (Q4_0 nibbles turned into signed bytes n - 8 on the way: elements
+// 0..15 of a block are the low halves of its bytes, 16..31 the high halves)
 // and both scale sets go through registers into a double-buffered LDS, one
 // step ahead; each wave multiplies BM/2 tokens x 64 rows (BM/64 x 2 tiles).
 // Tokens are the A operand and weight rows the B operand, so each lane's

@@ -2,9 +2,9 @@
 //
 // y[t][r] = sum_c W[r][c] * x[t][c] (Krafla ".mlb model, version 1" page,
 // "Body": rows are outputs).  The weights stay quantized in HBM and are
-// decoded in registers: Q4_0 byte j of a block holds element j in its low
-// nibble and element j + 16 in its high nibble, w = (nibble - 8) * d
-// (section "Q4_0"); Q8_0 w = q * d (section "Q8_0").
+// decoded in registers: a Q4_0 block keeps elements 0..15 in the low four
+// bits of its 16 bytes and elements 16..31 in the high four bits, w =
+// (nibble - 8) * d (section "Q4_0"); Q8_0 w = q * d (section "Q8_0").
 //
 // Work split: one wavefront owns NR consecutive rows.  Lane l reads the
 // 16-byte chunks l, l + 64, ... of each of its rows, so every load

@@ -8,11 +8,12 @@
  *   - two arrays, one after the other: q, the quants (Q8_0: rows*cols int8
  *     bytes; Q4_0: rows*cols/2 bytes), then d, one scale per block of 32
  *     consecutive weights of a row (f32, or IEEE f16 when scale_f16 = 1);
- *   - each array is zero-padded to a multiple of 64 bytes, so d starts at
- *     pad64(q bytes); the padding after d is optional;
+ *   - both arrays are padded with zeros up to a 64-byte boundary, so d
+ *     starts at pad64(q bytes); the padding after d may be absent;
  *   - Q8_0: w = q * d, and a quant byte of -128 is not allowed;
- *   - Q4_0: byte j of a block holds element j in its low nibble and element
- *     j + 16 in its high nibble; w = (nibble - 8) * d;
+ *   - Q4_0: the 16 bytes of a block carry elements 0..15 in their low four
+ *     bits and elements 16..31 in their high four bits, in order;
+ *     w = (nibble - 8) * d;
  *   - everything little-endian.
  * Conventions this library fixes where the page is silent: row r's blocks
  * (and scales) are consecutive, block k = r * (cols / 32) + c / 32; a
@@ -71,8 +72,9 @@ enum {
  * q_bytes = rows*cols (Q8_0) or rows*cols/2 (Q4_0); d_offset =
  * pad64(q_bytes); d_bytes = rows*cols/32 * (scale_f16 ? 2 : 4); min_span =
  * d_offset + d_bytes (the smallest buffer qmv_upload accepts).  Pure host
- * arithmetic in uint64_t with overflow checks ("All size arithmetic is
- * overflow-checked").  Any output pointer may be NULL.
+ * arithmetic in uint64_t; every sum and product is checked for overflow, as
+ * the page's "Validation done by the loader" section requires of a loader.
+ * Any output pointer may be NULL.
  * Errors: QMV_E_FORMAT (wtype, scale_f16), QMV_E_SHAPE (dimensions).
  */
 int qmv_span(uint32_t wtype, uint32_t scale_f16, uint32_t rows, uint32_t cols,
@@ -322,9 +324,10 @@ int qmv_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d,
  *     L = -6.0, -6.2, ..., -8.4; levels rint(x * (L / mx)) (half to even)
  *     clamped to [-8, 7]; d = sum w x l / sum w l^2 with w = x^2, summed in
  *     element order; the candidate of smallest sum w (x - d l)^2 wins, the
- *     first on ties; a block whose largest magnitude is below 1e-6 is
- *     divided by it first and d multiplied back; nibble = level + 8; with
- *     f16 scales the fitted d is rounded to f16.
+ *     first on ties; the values of a block whose largest magnitude is
+ *     under 1e-6 are divided by that magnitude before the fit and d is
+ *     multiplied by it after; nibble = level + 8; an f16 d is the fitted d
+ *     rounded to f16.
  * rule: QMV_Q4_ROUND (0) for every storage type, QMV_Q4_SEARCH (1) for
  * Q4_0 only.
  * image (device, 16-byte aligned, at least min_span bytes) receives the

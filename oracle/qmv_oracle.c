@@ -14,8 +14,8 @@
  *     weights of a row; f32, or IEEE f16 when scale_f16 is 1) and the
  *     64-byte zero padding of each array;
  *   - "Q8_0" (w = q x d, a byte of -128 is rejected);
- *   - "Q4_0" (byte j of a block holds element j in the low nibble and
- *     element j+16 in the high nibble, w = (nibble - 8) x d);
+ *   - "Q4_0" (elements 0..15 of a block in the low four bits of its 16
+ *     bytes, elements 16..31 in the high four bits, w = (nibble - 8) x d);
  *   - "Quantization rule" (activation quantizer, exact float32 operations);
  *   - the header table ("wtype", "scale_f16", "q8_mask", "shared_classifier")
  *     and the q8_mask class-bit paragraph;
@@ -227,8 +227,8 @@ void orc_product(const uint8_t *img, uint32_t wtype, uint32_t scale_f16,
 }
 
 /*
- * Feed-forward activation of the .mlb header field "act" (0 = SiLU, 1 = GELU
- * with the tanh approximation, the Gemma convention), in binary64:
+ * Feed-forward activation of the .mlb header field "act" (code 0 selects
+ * SiLU, code 1 the tanh form of GELU, the Gemma convention), in binary64:
  *   SiLU(a) = a / (1 + e^-a)   (a times the logistic sigmoid);
  *   GELU(a) = a/2 * (1 + tanh(u)),  u = sqrt(2/pi) * (a + 0.044715 a^3)
  *             (Hendrycks and Gimpel's tanh approximation of a * Phi(a)),
@@ -253,13 +253,14 @@ void orc_gated(const double *y1, const double *y3, uint64_t n, uint32_t act, dou
 }
 
 /*
- * Activation quantizer ("Quantization rule"), per block of 32, in float32
- * operations in the page's order:
- *   amax = max |x|;  amax < 1e-30 -> d = 0, q = 0;
- *   else d = amax / 127, q = trunc(x * (127 / amax) + copysign(0.5, x)),
- *   clamped to [-127, 127].
- * Each operation is rounded on its own (no fused multiply-add).  n must be a
- * multiple of 32.
+ * Activation quantizer (the .mlb page, "Quantization rule" section), per
+ * block of 32 values, in float32: the block's scale is its largest
+ * magnitude divided by 127 (zero, with all codes zero, when that magnitude
+ * is below 1e-30); each code is the value times the reciprocal of the scale
+ * (127 over the largest magnitude), rounded to the nearest integer with
+ * halves away from zero, and kept within [-127, 127].  The operations come
+ * in the order the section gives them, each rounded on its own (no fused
+ * multiply-add).  n must be a multiple of 32.
  */
 void orc_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d) {
     for (uint64_t b = 0; b < n / 32; ++b) {

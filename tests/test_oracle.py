@@ -177,7 +177,8 @@ def test_class_rule_hand_cases():
     # A Q8_0 file stores every class as Q8_0 (its q8_mask is 0).
     for cls in (1, 2, 4, 8, 16, 32, 64):
         assert O.class_wtype(Q8, 0, cls, 0) == ("ok", Q8)
-    # Shared classifier: tok_emb is Q8_0 if bit 1 or bit 2 is set.
+    # Shared classifier: the embedding table is stored as Q8_0 when q8_mask
+    # has bit 1 or bit 2.
     assert O.class_wtype(Q4, 2, 1, 1) == ("ok", Q8)
     assert O.class_wtype(Q4, 1, 1, 1) == ("ok", Q8)
     assert O.class_wtype(Q4, 4, 1, 1) == ("ok", Q4)

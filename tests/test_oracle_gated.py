@@ -1,6 +1,6 @@
 """Pins of the oracle's gated feed-forward output h = act(W1 x) * (W3 x)
-(the .mlb page's header field "act": 0 = SiLU, 1 = GELU with the tanh
-approximation; w1 = gate, w3 = up in its body table).
+(the .mlb page's header field "act": code 0 selects SiLU, code 1 the tanh
+form of GELU; w1 = gate, w3 = up in its body table).
 
 The activations are pinned to facts outside the oracle's own formulas:
 library routines (scipy's logistic function and normal CDF), the identity

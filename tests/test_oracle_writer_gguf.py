@@ -109,8 +109,8 @@ def test_f16_rounding_matches_numpy():
 
 
 def test_q8_f32_writer_is_the_activation_quantizer():
-    # the .mlb page: "Both the writer and the runtime's activation quantizer
-    # use these exact float32 operations"
+    # the .mlb page, "Quantization rule": the Q8_0 writer and the runtime's
+    # activation quantizer share the same float32 steps
     g = np.random.default_rng(7)
     R, C = 9, 256
     w = (g.standard_normal((R, C)) * np.exp(g.uniform(-80, 30, (R, 1)))).astype(np.float32)
