@@ -15,7 +15,7 @@
 //   - Q8_0 with f32 scales: the quantization rule, the same kernel as the
 //     activation quantizer (the page uses one rule for both);
 //   - Q8_0 with f16 scales: d = fl16(amax / 127), q = trunc(x * (1 / d) +
-//     copysign(0.5, x)) against that rounded d, clamped to [-127, 127]; a d
+//     copysign(0.5, x)) with d as rounded, clamped to [-127, 127]; a d
 //     above 65504 cannot be stored;
 //   - Q4_0 "round" rule: d = (first element of largest magnitude) / -8,
 //     nibble = min(15, trunc(x * (1 / d) + 8.5)), 1 / d taken as 0 when

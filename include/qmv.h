@@ -312,7 +312,7 @@ int qmv_quantize_q8(const float *x, uint64_t n, int8_t *q, float *d,
  *   - Q8_0, f32 scales: exactly qmv_quantize_q8 (the page uses one rule
  *     for the writer and the activation quantizer);
  *   - Q8_0, f16 scales: d = amax / 127 rounded to the nearest f16, then
- *     q = trunc(x * (1 / d) + copysign(0.5, x)) against that rounded d,
+ *     q = trunc(x * (1 / d) + copysign(0.5, x)) with d as rounded,
  *     clamped to [-127, 127] (q = 0 when d rounds to 0);
  *   - Q4_0, rule QMV_Q4_ROUND, the page's "round" rule: d = (the first
  *     element of largest magnitude) / -8, nibble = min(15, trunc(x * (1 /

@@ -462,7 +462,7 @@ int orc_gguf_to_image(uint32_t wtype, uint64_t rows, uint64_t cols,
  * operations rounded one at a time:
  *   - Q8_0, f32 scales: the quantization rule itself (orc_quantize_q8);
  *   - Q8_0, f16 scales: d = amax / 127 rounded to the nearest f16, then
- *     q = trunc(x * (1 / d) + copysign(0.5, x)) against that rounded d,
+ *     q = trunc(x * (1 / d) + copysign(0.5, x)) with d as rounded,
  *     clamped to [-127, 127]; a d above 65504 cannot be stored and is
  *     refused;
  *   - Q4_0, "round" rule (the rounding the page attributes to llama.cpp):
@@ -474,7 +474,7 @@ int orc_gguf_to_image(uint32_t wtype, uint64_t rows, uint64_t cols,
  * (every nibble 8, every weight 0), as llama.cpp does, and so does one whose
  * 1 / d overflows (|d| < 2^-128, weights below 2^-125); the Q4_0 levels use
  * the float32 d also when the stored scale is its f16 rounding (only the
- * Q8_0 sentence says "against that rounded d"); an f16 Q8_0 scale that
+ * Q8_0 rule names the rounded d for the codes); an f16 Q8_0 scale that
  * rounds to 0 from amax >= 1e-30 gives q = 0 (every weight is 0 either
  * way); the f16 rounding is the oracle's own round-to-nearest-even of the
  * float32 value; a Q4_0 f16 scale above 65504 is refused like a Q8_0 one.
