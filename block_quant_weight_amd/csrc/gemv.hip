@@ -248,26 +248,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // Activations as digits.  A workgroup first converts the activations, per
 // block of 32 consecutive values (the span of one weight scale): with E the
 // binary exponent of the block's largest magnitude (amax in [2^(E-1), 2^E)),
-// each value becomes the integer X = rne(x * 2^(22-E)), |X| <= 2^22, so x is
-// kept to within 2^(E-23) <= amax * 2^-22.  X is split into three signed
-// base-256 digits, X = D0 + 256 D1 + 65536 D2 with Dk in [-128, 127], and
-// each digit plane is stored as packed int8, so that v_dot4_i32_i8 multiplies
-// four weight codes by four digits exactly.  A block then adds
-//     d * 2^(E-22) * (T0 + 256 T1 + 65536 T2),   Tk = sum_j v_j Dk_j,
-// to its row, where the Tk are exact int32 sums (|Tk| < 2^18) and the blocks
-// are accumulated in float32.  Q8_0 quants are used as they are (signed
-// int8); a Q4_0 nibble n enters as the unsigned byte n and the -8 offset as
-// the exact starting value -8 * sum_j Dk_j of each Tk.  Zero weights give
-// exactly zero; a non-finite activation makes its block's scale NaN.
+// each value becomes the integer X = rne(x * 2^(30-E)), |X| <= 2^30, so x is
+// kept to within 2^(E-31) <= amax * 2^-30.  X is split into four signed
+// base-256 digits, X = D0 + 256 D1 + 65536 (D2 + 256 D3) with Dk in
+// [-128, 127], and each digit plane is stored as packed int8, so that
+// v_dot4_i32_i8 multiplies four weight codes by four digits exactly.  A block
+// then adds
+//     d * 2^(E-30) * (L + 65536 H),   L = T0 + 256 T1,  H = T2 + 256 T3,
+//     Tk = sum_j v_j Dk_j,
+// to its row, where L and H are exact int32 sums and the blocks are
+// accumulated in float32.  Q8_0 quants are used as they are (signed int8); a
+// Q4_0 nibble n enters as the unsigned byte n and the -8 offset as the exact
+// starting values -8 * sum_j (D0_j + 256 D1_j) and -8 * sum_j (D2_j + 256 D3_j).
+// Zero weights give exactly zero; a non-finite activation makes its block's
+// scale NaN.
 //
-// Small activations.  A nonzero value with |X| < 2^9 would keep fewer than
-// 10 significant bits, so it is not put in the digits (X = 0 there); a
-// 32-bit mask per chunk marks it, and after the chunk's digit sums each row
-// adds d * (v_j * x_j) in float32 for every marked j, in ascending order,
-// with x_j the activation itself.  Every other value keeps |X| >= 2^9, a
-// relative error of at most 2^-10, so each output is within about 2^-10 of
-// sum |w| |x| whatever the spread of a block's values.  For N(0,1) data
-// about 0.04% of the values are small.
+// Small activations.  A nonzero value with |X| < 2^9 (below about 2^-21 of
+// its block's largest) would keep fewer than 10 significant bits, so it is
+// not put in the digits (X = 0 there); a 32-bit mask per chunk marks it, and
+// after the digit sums of all its chunks each row adds d * (v_j * x_j) in
+// float32 for every marked j, in ascending order, with x_j the activation
+// itself.  Every other value keeps |X| >= 2^9, a relative error of at most
+// 2^-10, so each output is within about 2^-10 of sum |w| |x| whatever the
+// spread of a block's values.  For N(0,1) data about one value in 10^6 is
+// small, so a launch almost never takes that pass.
 //
 // Work split: one wavefront owns NR consecutive rows; lane l reads the 16-byte
 // chunks l, l + 64, ... of each row (a Q4_0 chunk is a whole block, a Q8_0
@@ -281,11 +285,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 //
 // LDS layout per activation vector, for chunk c = l + 64k:
 //   digit piece p (16 bytes = 16 digits of one plane) at ((k*P + p)*64 + l),
-//     Q4_0: P = 6, piece 2*plane + half; Q8_0: P = 3, piece = plane;
-//   then the block info at (k*64 + l): Q4_0 {-8*sum D0, -8*sum D1, -8*sum D2,
-//   2^(E-22)} as 16 bytes, Q8_0 2^(E-22) as 4 bytes; then the small-value
-//   mask (4 bytes) and two float slots (8 bytes, the streaming kernel's copy
-//   of the first small values) per chunk.
+//     Q4_0: P = 8, piece 2*plane + half; Q8_0: P = 4, piece = plane;
+//   then the block info at (k*64 + l): Q4_0 {-8*sum (D0 + 256 D1),
+//   -8*sum (D2 + 256 D3), 2^(E-30), small-value mask} as 16 bytes, Q8_0
+//   {2^(E-30), small-value mask} as 8 bytes.
 // A wave reading step k touches 64 consecutive 16-byte slots.
 // ---------------------------------------------------------------------------
 
@@ -310,45 +313,41 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <uint32_t WT>
 struct DigitLayout {
     static constexpr int CW = (WT == kQ4) ? 32 : 16;   // weights per 16-byte chunk
-    static constexpr int P = (WT == kQ4) ? 6 : 3;      // digit pieces per chunk
-    static constexpr int INFO = (WT == kQ4) ? 16 : 4;  // info bytes per chunk
+    static constexpr int P = (WT == kQ4) ? 8 : 4;      // digit pieces per chunk
+    static constexpr int INFO = (WT == kQ4) ? 16 : 8;  // info bytes per chunk
     // bytes of one staged activation vector with S steps of 64 chunks:
-    // digit pieces, block info, a 32-bit mask of small elements and two
-    // float slots for small values per chunk
-    static __host__ __device__ uint32_t vector_bytes(uint32_t S) {
-        return S * 64 * (P * 16 + INFO + 4 + 8);
-    }
-    static __host__ __device__ uint32_t mask_offset(uint32_t S) { return S * 64 * (P * 16 + INFO); }
-    static __host__ __device__ uint32_t slot_offset(uint32_t S) { return S * 64 * (P * 16 + INFO + 4); }
+    // digit pieces, then the block info per chunk
+    static __host__ __device__ uint32_t vector_bytes(uint32_t S) { return S * 64 * (P * 16 + INFO); }
 };
 
 __device__ __forceinline__ int dpp_swap_pair_i(int v) {
     return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
 }
 
-// Bytes [b0 b1 b2 .] of four words -> the three planes {b_k of w0..w3}.
-__device__ __forceinline__ void transpose3(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
-                                           uint32_t& p0, uint32_t& p1, uint32_t& p2) {
+// Bytes [b0 b1 b2 b3] of four words -> the four planes {b_k of w0..w3}.
+__device__ __forceinline__ void transpose4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                           uint32_t (&p)[4]) {
     // v_perm_b32: selector byte s picks byte s of the 64-bit {src0:src1}
     // (0..3 from src1, 4..7 from src0)
     const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0.0 w1.0 w0.1 w1.1
-    const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x06020602u);  // w0.2 w1.2 (twice)
+    const uint32_t b = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0.2 w1.2 w0.3 w1.3
     const uint32_t c = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2.0 w3.0 w2.1 w3.1
-    const uint32_t e = __builtin_amdgcn_perm(w3, w2, 0x06020602u);  // w2.2 w3.2 (twice)
-    p0 = __builtin_amdgcn_perm(c, a, 0x05040100u);                   // w0.0 w1.0 w2.0 w3.0
-    p1 = __builtin_amdgcn_perm(c, a, 0x07060302u);                   // w0.1 w1.1 w2.1 w3.1
-    p2 = __builtin_amdgcn_perm(e, b, 0x05040100u);                   // w0.2 w1.2 w2.2 w3.2
+    const uint32_t e = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2.2 w3.2 w2.3 w3.3
+    p[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);                 // w0.0 w1.0 w2.0 w3.0
+    p[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);                 // w0.1 w1.1 w2.1 w3.1
+    p[2] = __builtin_amdgcn_perm(e, b, 0x05040100u);                 // w0.2 w1.2 w2.2 w3.2
+    p[3] = __builtin_amdgcn_perm(e, b, 0x07060302u);                 // w0.3 w1.3 w2.3 w3.3
 }
 
 // Converts half block j (16 activations in xv; j even = first half) and
 // stores its digit pieces and, from the even lane, its block info.  The two
 // halves of a block sit in adjacent lanes of one wave, which exchange their
 // largest magnitude and digit sums.  `dig` and `info` point at the vector's
-// LDS area; h is the half block's index within its vector.
-template <uint32_t WT, bool SLOTS>
+// LDS area; h is the half block's index within its vector.  Returns true if
+// the half block holds a small value (below).
+template <uint32_t WT>
 __device__ __forceinline__ bool stage_half(const float4 (&xv)[4], uint32_t h,
-                                           int4* __restrict__ dig, void* __restrict__ info,
-                                           uint32_t* __restrict__ masks, float2* __restrict__ slots) {
+                                           int4* __restrict__ dig, void* __restrict__ info) {
     using L = DigitLayout<WT>;
     const float v[16] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w, xv[1].x, xv[1].y, xv[1].z, xv[1].w,
                          xv[2].x, xv[2].y, xv[2].z, xv[2].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w};
@@ -360,115 +359,113 @@ __device__ __forceinline__ bool stage_half(const float4 (&xv)[4], uint32_t h,
     m = max(m, static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(m))));
     const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
     const float sx = m >= 0x7F800000u ? __builtin_bit_cast(float, 0x7FC00000u)
-                                      : __builtin_amdgcn_ldexpf(1.0f, E - 22);
-    // X + 0x808080 in the low three bytes: rne(x * 2^(22-E)) by adding
-    // 1.5 * 2^23, whose bits are then 0x4B400000 + X.  A nonzero value whose
-    // X is below 2^9 in magnitude would keep less than 10 significant bits:
-    // such a ("small") value is left out of the digits (X = 0 there), marked
-    // in the chunk's mask, and its product added in float32 from the
-    // activation itself after the digit sums.
-    // With SLOTS, the first two small values of the half block are kept as
-    // floats too.
+                                      : __builtin_amdgcn_ldexpf(1.0f, E - 30);
+    // X = rne(x * 2^(30-E)) (exact scaling, then a round to integer), biased
+    // by 128 in each of its four bytes.  A nonzero value whose X is below
+    // 2^9 in magnitude would keep less than 10 significant bits: such a
+    // ("small") value is left out of the digits (X = 0 there), marked in the
+    // chunk's mask, and its product added in float32 from the activation
+    // itself after the digit sums.
     uint32_t u[16];
     uint32_t small = 0;
-    float f0 = 0.f, f1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float t = __builtin_amdgcn_ldexpf(v[i], 22 - E) + 12582912.0f;
-        const uint32_t ui = __builtin_bit_cast(uint32_t, t) - 0x4ABF7F80u;
-        const bool sm = (ui - (0x808080u - 511u)) < 1023u &&
+        const int X = static_cast<int>(__builtin_rintf(__builtin_amdgcn_ldexpf(v[i], 30 - E)));
+        const bool sm = static_cast<uint32_t>(X + 511) < 1023u &&
                         (__builtin_bit_cast(uint32_t, v[i]) << 1) != 0u;
-        if constexpr (SLOTS) {
-            f1 = sm && small != 0 && (small & (small - 1)) == 0 ? v[i] : f1;
-            f0 = sm && small == 0 ? v[i] : f0;
-        }
         small |= sm ? (1u << i) : 0u;
-        u[i] = sm ? 0x808080u : ui;
+        u[i] = sm ? 0x80808080u : static_cast<uint32_t>(X) + 0x80808080u;
     }
-    uint32_t pl[3][4];
+    uint32_t pl[4][4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        transpose3(u[4 * g], u[4 * g + 1], u[4 * g + 2], u[4 * g + 3], pl[0][g], pl[1][g],
-                   pl[2][g]);
+        uint32_t p[4];
+        transpose4(u[4 * g], u[4 * g + 1], u[4 * g + 2], u[4 * g + 3], p);
 #pragma unroll
-        for (int dd = 0; dd < 3; ++dd) pl[dd][g] ^= 0x80808080u;  // byte + 128 -> signed digit
+        for (int dd = 0; dd < 4; ++dd) pl[dd][g] = p[dd] ^ 0x80808080u;  // byte + 128 -> signed digit
     }
     if constexpr (WT == kQ4) {
         const uint32_t c = h >> 1, half = h & 1, k = c >> 6, l = c & 63;
 #pragma unroll
-        for (int dd = 0; dd < 3; ++dd)
+        for (int dd = 0; dd < 4; ++dd)
             dig[(k * L::P + 2 * dd + half) * 64 + l] =
                 make_int4(pl[dd][0], pl[dd][1], pl[dd][2], pl[dd][3]);
-        int s[3];
+        int sd[4];
 #pragma unroll
-        for (int dd = 0; dd < 3; ++dd) {
+        for (int dd = 0; dd < 4; ++dd) {
             int a = 0;
 #pragma unroll
             for (int g = 0; g < 4; ++g) a = __builtin_amdgcn_sdot4(pl[dd][g], 0x01010101, a, false);
-            s[dd] = a + dpp_swap_pair_i(a);
+            sd[dd] = a + dpp_swap_pair_i(a);
         }
         // the block's mask: element 16 * half + i of the block is bit
         // 16 * half + i
         const uint32_t mine = small << (16 * half);
         const uint32_t both = mine | static_cast<uint32_t>(dpp_swap_pair_i(static_cast<int>(mine)));
-        // slot h of the block: the half block's first small value
-        const float other = __builtin_bit_cast(float, dpp_swap_pair_i(__builtin_bit_cast(int, f0)));
-        if (half == 0) {
+        if (half == 0)
             static_cast<int4*>(info)[k * 64 + l] =
-                make_int4(-8 * s[0], -8 * s[1], -8 * s[2], __builtin_bit_cast(int, sx));
-            masks[k * 64 + l] = both;
-            if constexpr (SLOTS) slots[k * 64 + l] = make_float2(f0, other);
-        }
+                make_int4(-8 * (sd[0] + 256 * sd[1]), -8 * (sd[2] + 256 * sd[3]),
+                          __builtin_bit_cast(int, sx), static_cast<int>(both));
     } else {
         const uint32_t c = h, k = c >> 6, l = c & 63;
 #pragma unroll
-        for (int dd = 0; dd < 3; ++dd)
+        for (int dd = 0; dd < 4; ++dd)
             dig[(k * L::P + dd) * 64 + l] = make_int4(pl[dd][0], pl[dd][1], pl[dd][2], pl[dd][3]);
-        static_cast<float*>(info)[k * 64 + l] = sx;
-        masks[k * 64 + l] = small;
-        if constexpr (SLOTS) slots[k * 64 + l] = make_float2(f0, f1);
+        static_cast<uint2*>(info)[k * 64 + l] = make_uint2(__builtin_bit_cast(uint32_t, sx), small);
     }
     return small != 0;
 }
 
-// Code of element j of a 16-byte chunk as a float: Q4_0 nibble - 8 (element
-// j from byte j % 16, low nibble for j < 16), Q8_0 the signed byte j.
+// The small-value mask of chunk slot `is` of a vector's block info.
 template <uint32_t WT>
-__device__ __forceinline__ float chunk_code(const uint4 q, uint32_t j) {
-    const uint32_t byte = WT == kQ4 ? (j & 15u) : j;
-    const uint32_t wi = byte >> 2;
-    const uint32_t w = wi == 0 ? q.x : wi == 1 ? q.y : wi == 2 ? q.z : q.w;
-    const uint32_t sh = 8 * (byte & 3u) + (WT == kQ4 ? 4 * (j >> 4) : 0);
-    if constexpr (WT == kQ4) return static_cast<float>(static_cast<int>((w >> sh) & 15u) - 8);
-    else return static_cast<float>(static_cast<int8_t>((w >> sh) & 0xFFu));
+__device__ __forceinline__ uint32_t chunk_mask(const uint8_t* __restrict__ info, uint32_t is) {
+    if constexpr (WT == kQ4) return static_cast<uint32_t>(reinterpret_cast<const int4*>(info)[is].w);
+    else return reinterpret_cast<const uint2*>(info)[is].y;
 }
 
-// Adds the small activations of one chunk (mask bits, left out of the digit
-// sums) of every row: acc[r] += d[r] * (v[r][j] * x_j), in ascending j.  x_j
-// comes from the chunk's two float slots if SLOTS (Q4_0: the first small
-// value of each half block; Q8_0: the first two), or else from xc in memory.
-template <uint32_t WT, bool SF16, bool SLOTS, int NR, int SMAX>
-__device__ __forceinline__ void small_rows(const uint4 (&qv)[NR][SMAX], const uint32_t (&dv)[NR][SMAX],
-                                           int k, uint32_t mask, const float2* __restrict__ slot,
-                                           const float* __restrict__ xc, float (&acc)[NR]) {
-    if (mask == 0) return;
-    const float2 sv = SLOTS ? *slot : make_float2(0.f, 0.f);
-    uint32_t used = 0;  // slots taken
-    while (mask != 0) {
-        const uint32_t j = __builtin_ctz(mask);
-        mask &= mask - 1;
-        // the slot this value may sit in
-        const uint32_t want = WT == kQ4 ? 1u + (j >> 4) : (used == 0 ? 1u : 2u);
-        float xj;
-        if (SLOTS && (used & want) == 0 && (WT == kQ4 || used != 3u)) {
-            xj = want == 1u ? sv.x : sv.y;
-            used |= want;
-        } else {
-            xj = xc[j];
-        }
+// Adds the small activations of one step (mask bits, left out of the digit
+// sums) to the wave-reduced row sums: sum[r] += d * (v_j * x_j) for each
+// small element j of each chunk c of the step, in ascending c and j, with
+// x_j read from xs (the activations of the step's first chunk).  mask_l is
+// the lane's own chunk's mask (zero past the row).  The walk is
+// wave-uniform: the quants and the scale of chunk c are read from lane c
+// with readlane.
+template <uint32_t WT, bool SF16, int NR, int SMAX>
+__device__ __forceinline__ void small_sums(const uint4 (&qv)[NR][SMAX], const uint32_t (&dv)[NR][SMAX],
+                                           int k, uint32_t mask_l, const float* __restrict__ xs,
+                                           float (&sum)[NR]) {
+    constexpr uint32_t CW = DigitLayout<WT>::CW;
+    uint64_t chunks = __ballot(mask_l != 0u);
+    while (chunks != 0) {
+        const uint32_t c = static_cast<uint32_t>(__builtin_ctzll(chunks));
+        chunks &= chunks - 1;
+        uint32_t mask = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mask_l), c));
+        uint32_t qw[NR][4], db[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-            acc[r] = fmaf(scale_from_bits<SF16>(dv[r][k]), chunk_code<WT>(qv[r][k], j) * xj, acc[r]);
+        for (int r = 0; r < NR; ++r) {
+            qw[r][0] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qv[r][k].x), c));
+            qw[r][1] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qv[r][k].y), c));
+            qw[r][2] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qv[r][k].z), c));
+            qw[r][3] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(qv[r][k].w), c));
+            db[r] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dv[r][k]), c));
+        }
+        while (mask != 0) {
+            const uint32_t j = __builtin_ctz(mask);
+            mask &= mask - 1;
+            const float xj = xs[c * CW + j];
+            // element j: Q4_0 nibble of byte j % 16 (high half for j >= 16),
+            // Q8_0 byte j
+            const uint32_t byte = WT == kQ4 ? (j & 15u) : j;
+            const uint32_t sh = 8 * (byte & 3u) + (WT == kQ4 ? 4 * (j >> 4) : 0);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint32_t w = qw[r][byte >> 2];
+                const float code = WT == kQ4
+                    ? static_cast<float>(static_cast<int>((w >> sh) & 15u) - 8)
+                    : static_cast<float>(static_cast<int8_t>((w >> sh) & 0xFFu));
+                sum[r] = fmaf(scale_from_bits<SF16>(db[r]), code * xj, sum[r]);
+            }
+        }
     }
 }
 
@@ -484,20 +481,22 @@ __device__ __forceinline__ bool barrier_any(bool mine, uint32_t* slots, uint32_t
     return any != 0;
 }
 
-// T0 + 256 T1 + 65536 T2 in float32 (T1 + 256 T2 is exact in int32).
-__device__ __forceinline__ float combine_digits(int t0, int t1, int t2) {
-    const int hi = t1 + t2 * 256;
-    return fmaf(static_cast<float>(hi), 256.f, static_cast<float>(t0));
+// T0 + 256 T1 + 65536 (T2 + 256 T3) in float32, from lo = T0 + 256 T1 and
+// hi = T2 + 256 T3 (each exact in int32).
+__device__ __forceinline__ float combine_digits(int lo, int hi) {
+    return fmaf(static_cast<float>(hi), 65536.f, static_cast<float>(lo));
 }
 
-// Digit sums of one Q4_0 chunk (a whole block) with quants w.
-__device__ __forceinline__ float q4_digit_dot(const uint4 w, const int4 (&pc)[6], const int4 info) {
+// Digit sums of one Q4_0 chunk (a whole block) with quants w; the -8 offset
+// enters as the starting values info.x (planes 0 and 1) and info.y (planes
+// 2 and 3).
+__device__ __forceinline__ float q4_digit_dot(const uint4 w, const int4 (&pc)[8], const int4 info) {
     uint32_t mask = 0x0F0F0F0Fu;
     asm("" : "+v"(mask));
     const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-    int t[3] = {info.x, info.y, info.z};
+    int t[4] = {info.x, 0, info.y, 0};
 #pragma unroll
-    for (int dd = 0; dd < 3; ++dd) {
+    for (int dd = 0; dd < 4; ++dd) {
         const int lo_d[4] = {pc[2 * dd].x, pc[2 * dd].y, pc[2 * dd].z, pc[2 * dd].w};
         const int hi_d[4] = {pc[2 * dd + 1].x, pc[2 * dd + 1].y, pc[2 * dd + 1].z, pc[2 * dd + 1].w};
 #pragma unroll
@@ -506,23 +505,23 @@ __device__ __forceinline__ float q4_digit_dot(const uint4 w, const int4 (&pc)[6]
             t[dd] = __builtin_amdgcn_sdot4(static_cast<int>((q[i] >> 4) & mask), hi_d[i], t[dd], false);
         }
     }
-    return combine_digits(t[0], t[1], t[2]);
+    return combine_digits(t[0] + 256 * t[1], t[2] + 256 * t[3]);
 }
 
 // Digit sums of one Q8_0 chunk (half a block) with quants w.
-__device__ __forceinline__ float q8_digit_dot(const uint4 w, const int4 (&pc)[3]) {
+__device__ __forceinline__ float q8_digit_dot(const uint4 w, const int4 (&pc)[4]) {
     const int q[4] = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
                       static_cast<int>(w.w)};
-    int t[3];
+    int t[4];
 #pragma unroll
-    for (int dd = 0; dd < 3; ++dd) {
+    for (int dd = 0; dd < 4; ++dd) {
         const int dg[4] = {pc[dd].x, pc[dd].y, pc[dd].z, pc[dd].w};
         int a = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) a = __builtin_amdgcn_sdot4(q[i], dg[i], a, false);
         t[dd] = a;
     }
-    return combine_digits(t[0], t[1], t[2]);
+    return combine_digits(t[0] + 256 * t[1], t[2] + 256 * t[3]);
 }
 
 // Adds one chunk of every row (quants qv[r][k], scale bits dv[r][k]) times
@@ -537,11 +536,11 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&qv)[NR][SMAX], const ui
     float sx;
     if constexpr (WT == kQ4) {
         const int4 in = reinterpret_cast<const int4*>(info)[is];
-        sx = __builtin_bit_cast(float, in.w);
+        sx = __builtin_bit_cast(float, in.z);
 #pragma unroll
         for (int r = 0; r < NR; ++r) t[r] = q4_digit_dot(qv[r][k], pc, in);
     } else {
-        sx = reinterpret_cast<const float*>(info)[is];
+        sx = __builtin_bit_cast(float, reinterpret_cast<const uint2*>(info)[is].x);
 #pragma unroll
         for (int r = 0; r < NR; ++r) t[r] = q8_digit_dot(qv[r][k], pc);
     }
@@ -636,15 +635,11 @@ __device__ __forceinline__ void oneshot_body(
     }
 
     // ---- 3. activations -> digits in LDS ----
-    const uint32_t mask_off = L::mask_offset(S);
-    constexpr bool SLOTS_ = false;  // small values read from memory
     bool mysmall = false;
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t b = j / nhalf, h = j - b * nhalf;
         uint8_t* base = lds + b * vec_bytes;
-        mysmall |= stage_half<WT, SLOTS_>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes,
-                                  reinterpret_cast<uint32_t*>(base + mask_off),
-                                  reinterpret_cast<float2*>(base + L::slot_offset(S)));
+        mysmall |= stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -662,45 +657,57 @@ __device__ __forceinline__ void oneshot_body(
     if (wrows == 0) return;  // uniform per wave, after the barrier
 
     // ---- 4. multiply ----
-    float acc[NB][NR];
+    auto multiply = [&](auto small_t) {
+        constexpr bool SMALL = decltype(small_t)::value;
+        float acc[NB][NR];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) acc[b][r] = 0.f;
+            for (int r = 0; r < NR; ++r) acc[b][r] = 0.f;
 #pragma unroll
-    for (int k = 0; k < SMAX; ++k) {
-        if (k < static_cast<int>(S)) {
-            const bool valid = lane + 64u * k < nchunks;
+        for (int k = 0; k < SMAX; ++k) {
+            if (k < static_cast<int>(S)) {
+                const bool valid = lane + 64u * k < nchunks;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint8_t* base = lds + b * vec_bytes;
-                const int4* dg = reinterpret_cast<const int4*>(base) + k * P * 64 + lane;
-                int4 pc[P];
+                for (int b = 0; b < NB; ++b) {
+                    const uint8_t* base = lds + b * vec_bytes;
+                    const int4* dg = reinterpret_cast<const int4*>(base) + k * P * 64 + lane;
+                    int4 pc[P];
 #pragma unroll
-                for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
-                chunk_rows<WT, SF16, NR>(qv, dv, k, pc, base + dig_bytes, k * 64 + lane, valid,
-                                         acc[b]);
-                // then the chunk's small activations, left out of the digits
-                // (a workgroup without any skips this)
-                if (any_small) {
-                    const uint32_t* mk = reinterpret_cast<const uint32_t*>(base + mask_off);
-                    const uint32_t mask = valid ? mk[k * 64 + lane] : 0u;
-                    small_rows<WT, SF16, false, NR>(
-                        qv, dv, k, mask,
-                        reinterpret_cast<const float2*>(base + L::slot_offset(S)) + k * 64 + lane,
-                        x + static_cast<uint64_t>(b) * cols + (lane + 64u * k) * CW, acc[b]);
+                    for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
+                    chunk_rows<WT, SF16, NR>(qv, dv, k, pc, base + dig_bytes, k * 64 + lane, valid,
+                                             acc[b]);
                 }
             }
         }
-    }
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
+            float sum[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float sum = wave_reduce(acc[b][r]);
-            if (lane == 0 && static_cast<uint32_t>(r) < wrows)
-                y[static_cast<uint64_t>(b) * rows + row0 + r] = sum;
+            for (int r = 0; r < NR; ++r) sum[r] = wave_reduce(acc[b][r]);
+            // then the small activations, left out of the digits, in
+            // ascending order (every quant has arrived: the reads of x here
+            // wait for nothing else)
+            if constexpr (SMALL) {
+                const uint8_t* info = lds + b * vec_bytes + dig_bytes;
+#pragma unroll
+                for (int k = 0; k < SMAX; ++k) {
+                    if (k < static_cast<int>(S)) {
+                        const uint32_t mask =
+                            lane + 64u * k < nchunks ? chunk_mask<WT>(info, k * 64 + lane) : 0u;
+                        small_sums<WT, SF16, NR>(qv, dv, k, mask,
+                                                 x + static_cast<uint64_t>(b) * cols + 64u * k * CW, sum);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (lane == 0 && static_cast<uint32_t>(r) < wrows)
+                    y[static_cast<uint64_t>(b) * rows + row0 + r] = sum[r];
         }
+    };
+    if (any_small) multiply(std::true_type{});
+    else multiply(std::false_type{});
 }
 
 template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, int WAVES>
@@ -865,7 +872,8 @@ template <uint32_t WT, bool SF16, int NR, int NB, int SMAX, bool GATED, bool SMA
 __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<NR, SMAX>& b,
                                              const uint8_t* __restrict__ lds,
                                              const float* __restrict__ x, uint32_t cols,
-                                             uint32_t S, uint32_t lane, uint32_t act) {
+                                             uint32_t S, uint32_t lane, uint32_t act,
+                                             uint32_t steps_small) {
     using L = DigitLayout<WT>;
     constexpr int P = L::P;
     const uint32_t nchunks = cols / L::CW;
@@ -889,42 +897,43 @@ __device__ __forceinline__ void compute_tile(const TileArgs& g, const TileRegs<N
                 for (int p = 0; p < P; ++p) pc[p] = dg[p * 64];
                 chunk_rows<WT, SF16, NR>(b.q, b.d, k, pc, base + dig_bytes, k * 64 + lane, valid,
                                          acc[v]);
-                // then the chunk's small activations (the one-shot kernel's
-                // order, so that both give the same sums)
-                if constexpr (SMALL) {
-                    const uint32_t* mk =
-                        reinterpret_cast<const uint32_t*>(base + L::mask_offset(S));
-                    const uint32_t mask = valid ? mk[k * 64 + lane] : 0u;
-                    small_rows<WT, SF16, true, NR>(
-                        b.q, b.d, k, mask,
-                        reinterpret_cast<const float2*>(base + L::slot_offset(S)) + k * 64 + lane,
-                        x + static_cast<uint64_t>(v) * cols + (lane + 64u * k) * L::CW, acc[v]);
-                }
             }
         }
     }
+    // the wave-reduced row sums, then the small activations (the one-shot
+    // kernel's order, so that both give the same sums) on the steps that
+    // hold any (bit v * SMAX + k of steps_small), then the stores
     const uint32_t rows = g.rows[b.mat];
     float* y = g.y[b.mat];
-    if constexpr (GATED) {
-        constexpr int NH = NR / 2;
 #pragma unroll
-        for (int v = 0; v < NB; ++v)
+    for (int v = 0; v < NB; ++v) {
+        float sum[NR];
 #pragma unroll
-            for (int r = 0; r < NH; ++r) {
-                const float s1 = wave_reduce(acc[v][r]);
-                const float s3 = wave_reduce(acc[v][r + NH]);
-                if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
-                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = ffn_act(s1, act) * s3;
+        for (int r = 0; r < NR; ++r) sum[r] = wave_reduce(acc[v][r]);
+        if constexpr (SMALL) {
+            const uint8_t* info = lds + v * vec_bytes + dig_bytes;
+#pragma unroll
+            for (int k = 0; k < SMAX; ++k) {
+                if ((steps_small >> (v * SMAX + k)) & 1u) {
+                    const uint32_t mask =
+                        lane + 64u * k < nchunks ? chunk_mask<WT>(info, k * 64 + lane) : 0u;
+                    small_sums<WT, SF16, NR>(b.q, b.d, k, mask,
+                                             x + static_cast<uint64_t>(v) * cols + 64u * k * L::CW, sum);
+                }
             }
-    } else {
+        }
+        if constexpr (GATED) {
+            constexpr int NH = NR / 2;
 #pragma unroll
-        for (int v = 0; v < NB; ++v)
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                const float sum = wave_reduce(acc[v][r]);
+            for (int r = 0; r < NH; ++r)
                 if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
-                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = sum;
-            }
+                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = ffn_act(sum[r], act) * sum[r + NH];
+        } else {
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+                if (lane == 0 && static_cast<uint32_t>(r) < b.wrows)
+                    y[static_cast<uint64_t>(v) * rows + b.row0 + r] = sum[r];
+        }
     }
 }
 
@@ -980,15 +989,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     };
     load_any(tile(t), ra);
 
-    const uint32_t mask_off = L::mask_offset(S);
-    constexpr bool SLOTS_ = true;  // small values kept in LDS
     bool mysmall = false;
     auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
         const uint32_t v = j / nhalf, h = j - v * nhalf;
         uint8_t* base = lds + v * vec_bytes;
-        mysmall |= stage_half<WT, SLOTS_>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes,
-                                  reinterpret_cast<uint32_t*>(base + mask_off),
-                                  reinterpret_cast<float2*>(base + L::slot_offset(S)));
+        mysmall |= stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -1003,6 +1008,20 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     }
     __shared__ uint32_t small_slots[kStreamWaves];
     const bool any_small = barrier_any(mysmall, small_slots, kStreamWaves);
+    // bit v * SMAX + k: step k of vector v holds a small activation (the
+    // same for every tile, so found once)
+    static_assert(NB * SMAX <= 32, "one bit per vector and step");
+    uint32_t steps_small = 0;
+    if (any_small) {
+#pragma unroll
+        for (int v = 0; v < NB; ++v)
+#pragma unroll
+            for (int k = 0; k < SMAX; ++k) {
+                const bool has = k < static_cast<int>(S) && lane + 64u * k < cols / L::CW &&
+                                 chunk_mask<WT>(lds + v * vec_bytes + dig_bytes, k * 64 + lane) != 0u;
+                steps_small |= __ballot(has) != 0 ? (1u << (v * SMAX + k)) : 0u;
+            }
+    }
 
     // two register sets: the next tile's loads are in flight (the loop
     // without the small-activation pass unless a staged value is small)
@@ -1010,11 +1029,11 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
         constexpr bool W = decltype(small_t)::value;
         while (t < end) {
             load_any(tile(t + step), rb);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, ra, lds, x, cols, S, lane, act);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, ra, lds, x, cols, S, lane, act, steps_small);
             t += step;
             if (t >= end) break;
             load_any(tile(t + step), ra);
-            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, rb, lds, x, cols, S, lane, act);
+            compute_tile<WT, SF16, NR, NB, SMAX, GATED, W>(g, rb, lds, x, cols, S, lane, act, steps_small);
             t += step;
         }
     };
@@ -1079,7 +1098,7 @@ hipError_t gemv_oneshot_launch(const MatView& m, const float* x, float* y, size_
 // The one-shot kernel's limits: at most 16 steps of 64 chunks per row, the
 // staged activations in at most this much LDS, and a wave's rows within a
 // 32-bit buffer range.
-constexpr uint64_t kOneshotLds = 64 * 1024;
+constexpr uint64_t kOneshotLds = 72 * 1024;
 constexpr uint32_t kOneshotSteps = 16;
 
 template <uint32_t WT>

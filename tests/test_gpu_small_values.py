@@ -2,15 +2,15 @@
 the parity bar |y - ref| <= 2e-3 * sum |w||x| per output (the .mlb page's
 "Body" product; any finite activations are valid input).
 
-Each block of 32 holds one value 1.0, a number of "small" values (far below
-1.0: the kernels add their products in float32 after the block's digit
-sums) and zeros; the weight that meets the 1.0 is zero, so the output is
-carried by the small values alone and any loss of them shows at full size.
-The count of small values per block varies from 1 to 31, so the streaming
-kernel's two float slots per chunk and its memory path are both taken, as
-is the one-shot kernel's memory path.  A second pattern puts values just
-above and just below the threshold (2^-12 of the block's largest), where the
-fixed point keeps the fewest significant bits."""
+Each block of 32 holds one value 1.0, a number of values far below 1.0
+and zeros; the weight that meets the 1.0 is zero, so the output is carried
+by the far smaller values alone and any loss of them shows at full size.
+The count of such values per block varies from 1 to 31, and they include
+"small" ones (below 2^-20 of the block's largest, whose products the kernels
+add in float32 after the digit sums), so the one-shot and the streaming
+kernels take their small-value pass with up to 31 values per block.  A
+second pattern puts values just above and just below that threshold, where
+the fixed point keeps the fewest significant bits."""
 import numpy as np
 import pytest
 
@@ -85,7 +85,7 @@ def check(y, ref, norm, what):
 
 @pytest.mark.parametrize("wt,sf,R,C", SHAPES)
 @pytest.mark.parametrize("B", [1, 3])
-@pytest.mark.parametrize("mags", [(1e-7, 3e-6, 1e-5, 2e-4), (2.3e-4, 2.5e-4, 2.6e-4, 3e-4)],
+@pytest.mark.parametrize("mags", [(1e-12, 1e-7, 3e-6, 2e-4), (9.0e-7, 9.5e-7, 9.6e-7, 1.05e-6)],
                          ids=["far", "threshold"])
 def test_gemv_small_values(wt, sf, R, C, B, mags):
     x, big = small_pattern(B, C, 900 + R + B, np.array(mags))
