@@ -138,7 +138,7 @@ DOMINANT_KERNEL = {
     "decode_layer": ("gemv_stream_kernel (w1|w3)", "gemv.hip"),
     "decode_layer_gated": ("gemv_stream_kernel, gated (w1|w3)", "gemv.hip"),
     "decode_layer_7": ("gemv_oneshot_kernel (w2)", "gemv.hip"),
-    "lm_head_b1": ("gemv_oneshot_kernel", "gemv.hip"),
+    "lm_head_b1": ("gemv_oneshot_kernel_occ6", "gemv.hip"),
     "lm_head_b64": ("gemv_mfma_kernel (f16 operands)", "gemv_mfma.hip"),
     "gemm_q4_14336x4096": ("qmv_gemm call: stage_x_kernel + gemm_f16_kernel", "gemm.hip"),
     "gemm_q8_4096x14336": ("qmv_gemm call: stage_x_kernel + gemm_f16_kernel + "
