@@ -19,24 +19,27 @@
 // product, half the 2e-3 tolerance.
 //
 // Work split.  One workgroup of 8 waves per compute unit keeps up to 64
-// tokens of f16 activations in LDS (one row of 2*cols + 16 bytes per token,
-// the 16-byte pad spreading a wave's fragment reads over all banks).  Each
+// tokens of f16 activations in LDS (one row of 2*cols bytes per token, its
+// 16-byte chunks XOR-swizzled by the token's low four bits so that a wave's
+// fragment reads spread over all 64 banks).  Each
 // wave walks tiles of 32 weight rows; tokens are the A operand (two 32-token
 // tiles) and weight rows the B operand of v_mfma_f32_32x32x16_f16, so a
 // lane's output column is a weight row and stores of 32 consecutive rows per
 // token coalesce.  The B operand wants lane (r, h) = (lane % 32, lane / 32)
 // to hold 8 + 8 quants of row r (block j, half h); loading that directly
 // makes every load instruction touch 32 rows, which the address and L1 units
-// serve one lane at a time.  Instead a wave loads a pair of blocks of its 32
-// rows with two instructions of 16 rows x 64 contiguous bytes, writes them to
-// its own 2 KiB LDS slice (16-byte chunks XOR-swizzled by row so that both
-// the writes and the reads below are free of bank conflicts) and reads them
-// back in the operand layout.  The activations are read with the same split
-// of k, so A and B agree on which k each step sums.  Loads go by groups of 8
-// blocks (4 pairs of quant loads and one 16-byte load of a row's 8 scales) in
-// two register sets, the next group in flight while one is multiplied,
-// across tile boundaries; raw buffer loads past the wave's last group get an
-// out-of-range offset and return zeros, so the loads need no branches.
+// serve one lane at a time.  Instead a wave loads four blocks of its 32 rows
+// with four instructions of 8 rows x 128 contiguous bytes (whole cache
+// lines), writes them to its own 4 KiB LDS slice (16-byte chunks
+// XOR-swizzled by row so that both the writes and the reads below are free
+// of bank conflicts) and reads them back in the operand layout.  The
+// activations are read with the same split of k, so A and B agree on which k
+// each step sums.  Loads go by groups of 8 blocks (2 quads of quant loads
+// and one 16-byte load of a row's 8 scales) in two register sets, the next
+// group in flight while one is multiplied, across tile boundaries; raw
+// buffer loads past the wave's last group get an out-of-range offset and
+// return zeros, so the loads need no branches.  The per-token output scales
+// live in one register (lane t: token t) and are read with readlane.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -51,11 +54,16 @@ constexpr int kWaves = 8;
 constexpr int kTokens = 64;     // tokens per pass (two 32-token tiles)
 constexpr int kMaxCols = 1024;  // activations of one pass must fit LDS
 constexpr uint32_t kOob = 0xFFFFFFF0u;
-constexpr int kXBytes = kTokens * (2 * kMaxCols + 16);
-constexpr int kSlice = 32 * 64;  // a wave's LDS slice: 32 rows x one block pair
+constexpr int kXBytes = kTokens * 2 * kMaxCols;
+constexpr int kSlice = 32 * 128;  // a wave's LDS slice: 32 rows x four blocks
 // cache-policy bits of the output stores: non-temporal (measured 77.4 ->
 // 72.6-74.7 us for 248320 x 1024 at batch 64, bit-identical)
 constexpr int kStreamStore = 2;
+// cache-policy bits of the weight loads: non-temporal.  Each load
+// instruction takes whole 128-byte lines (8 rows x 128 bytes), so no line is
+// needed again after its load (with loads of half lines this policy was
+// slower: the other half was evicted before its load came).
+constexpr int kWeightLoad = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -97,17 +105,25 @@ __device__ __forceinline__ void dequant16(const u32x4 w, f16x2 dd, f16x8 (&out)[
         }
 }
 
-// Byte offset in a wave's slice of row n's 16-byte chunk c (0..3) of a block
-// pair: chunk index XORed with bits 1..2 of the row, so that 8 consecutive
-// lanes of either access pattern hit 8 different groups of four banks.
+// Byte offset in a wave's slice of row n's 16-byte chunk c (0..7) of four
+// blocks: chunk index XORed with the row's low three bits, so that 8
+// consecutive rows of either access pattern hit 8 different groups of four
+// banks.
 __device__ __forceinline__ uint32_t slice_off(uint32_t n, uint32_t c) {
-    return n * 64 + ((c ^ ((n >> 1) & 3)) << 4);
+    return n * 128 + ((c ^ ((n >> 1) & 7)) << 4);
 }
 
-// Loads of one group of 8 blocks (4 block pairs) of a tile: the quants, as
-// two 16-row x 64-byte loads per pair, and this lane's row's 8 scales.
+// Byte offset in the activations of token t's 16-byte chunk c (8 values),
+// XOR-swizzled the same way.
+__device__ __forceinline__ uint32_t x_off(uint32_t t, uint32_t c, uint32_t P) {
+    return t * P + ((c ^ (t & 15)) << 4);
+}
+
+// Loads of one group of 8 blocks of a tile: the quants, as two quads of four
+// blocks, each four loads of 8 rows x 128 contiguous bytes (whole cache
+// lines), and this lane's row's 8 scales.
 struct Group {
-    u32x4 q[4][2];
+    u32x4 q[2][4];
     u32x4 sc;
 };
 
@@ -120,10 +136,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
     static_assert(NG % 2 == 0, "groups alternate between two register sets within a tile");
     __shared__ __align__(16) uint8_t xs[kXBytes];
     __shared__ __align__(16) uint8_t wsl[kWaves * kSlice];
-    __shared__ float tinv[kTokens];
     const int tid = threadIdx.x, lane = tid & 63;
     const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    constexpr uint32_t P = 2 * cols + 16;  // LDS bytes per token
+    constexpr uint32_t P = 2 * cols;  // LDS bytes per token
     const uint32_t r = lane & 31, h = lane >> 5;
     uint8_t* slice = wsl + wid * kSlice;
 
@@ -152,12 +167,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
         // block then waits for its own quants only
         dst.sc = __builtin_amdgcn_raw_buffer_load_b128(gd, (base + r) * NJ * 2 + 16 * g, 0, 0);
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int qd = 0; qd < 2; ++qd)
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint32_t row = base + 16 * k + (lane >> 2);
-                const uint32_t off = row * cols + 256 * g + 64 * p + 16 * (lane & 3);
-                dst.q[p][k] = __builtin_amdgcn_raw_buffer_load_b128(gq, off, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t row = base + 8 * i + (lane >> 3);
+                const uint32_t off = row * cols + 256 * g + 128 * qd + 16 * (lane & 7);
+                dst.q[qd][i] = __builtin_amdgcn_raw_buffer_load_b128(gq, off, 0, kWeightLoad);
             }
     };
 
@@ -206,16 +221,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
                                       static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.y, sh))};
                     const f16x2 p1 = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.z, sh)),
                                       static_cast<_Float16>(__builtin_amdgcn_ldexpf(a.w, sh))};
-                    *reinterpret_cast<uint2*>(xs + t * P + 8 * c4) =
+                    *reinterpret_cast<uint2*>(xs + x_off(t, c4 >> 1, P) + 8 * (c4 & 1)) =
                         make_uint2(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1));
                 }
             }
+            // (the output scales pass through the start of the slices, free
+            // until the first group is multiplied)
             if (lane == 0)
-                tinv[t] = t >= ntok ? 0.f
-                        : finite ? __builtin_amdgcn_ldexpf(1.0f, -sh) * inv_wscale
-                                 : __builtin_bit_cast(float, 0x7FC00000u);
+                reinterpret_cast<float*>(wsl)[t] =
+                    t >= ntok ? 0.f
+                    : finite ? __builtin_amdgcn_ldexpf(1.0f, -sh) * inv_wscale
+                             : __builtin_bit_cast(float, 0x7FC00000u);
         }
     }
+    __syncthreads();
+    // lane t keeps token t's output scale (read back per store by bpermute)
+    const float tscale = reinterpret_cast<const float*>(wsl)[lane];
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t yrs = rsrc(y, ntok * rows * 4);
@@ -228,15 +249,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
     // multiplies group G (blocks 8g .. 8g + 7 of its tile) into acc
     auto run_group = [&](const Group& gr, uint32_t g) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            // pair p to the slice in the loaded layout, then back per block
+        for (int qd = 0; qd < 2; ++qd) {
+            // quad qd to the slice in the loaded layout, then back per block
             // in the operand layout
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                *reinterpret_cast<u32x4*>(slice + slice_off(16 * k + (lane >> 2), lane & 3)) = gr.q[p][k];
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x4*>(slice + slice_off(8 * i + (lane >> 3), lane & 7)) = gr.q[qd][i];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int jj = 2 * p + b;          // block within the group
+            for (int b = 0; b < 4; ++b) {
+                const int jj = 4 * qd + b;         // block within the group
                 const uint32_t j = 8 * g + jj;     // block within the row
                 const u32x4 w = *reinterpret_cast<const u32x4*>(slice + slice_off(r, 2 * b + h));
                 const uint32_t sbits = gr.sc[jj / 2] >> (16 * (jj % 2));
@@ -248,9 +269,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
                 f16x8 xf[2][2];
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const uint8_t* xp = xs + (32 * mt + r) * P + 2 * (32 * j + 16 * h);
-                    xf[mt][0] = *reinterpret_cast<const f16x8*>(xp);
-                    xf[mt][1] = *reinterpret_cast<const f16x8*>(xp + 16);
+                    const uint32_t t = 32 * mt + r, c = 4 * j + 2 * h;
+                    xf[mt][0] = *reinterpret_cast<const f16x8*>(xs + x_off(t, c, P));
+                    xf[mt][1] = *reinterpret_cast<const f16x8*>(xs + x_off(t, c + 1, P));
                 }
 #pragma unroll
                 for (int k = 0; k < 2; ++k)
@@ -273,7 +294,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_mfma_kernel(
                 const uint32_t off = (rok && t < ntok) ? (t * rows + row) * 4 : kOob;
                 // the store takes the 32-bit pattern (an unsigned int);
                 // non-temporal: the logits are not read again here
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[mt][e] * tinv[t]),
+                // token t = t0 + 4h: the scales of both halves by readlane
+                // (a constant lane each), then a select
+                const int t0 = 32 * mt + 8 * (e / 4) + (e % 4);
+                const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tscale), t0));
+                const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tscale), t0 + 4));
+                const float ts = h ? s1 : s0;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, acc[mt][e] * ts),
                                                       yrs, off, 0, kStreamStore);
                 acc[mt][e] = 0.f;
             }
