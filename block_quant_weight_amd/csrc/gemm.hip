@@ -222,6 +222,26 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const void* __restrict__ x
 namespace mm {
 
 constexpr int kThreads = 512;
+
+// floor(2^32 / n) + 1 (n >= 2; 0 for n = 1): for every 32-bit i,
+// __umulhi(i, that) is i / n or one more, since that exceeds 2^32 / n by at
+// most 1.
+inline uint32_t reciprocal(uint32_t n) {
+    return n < 2 ? 0u : static_cast<uint32_t>((uint64_t{1} << 32) / n + 1);
+}
+
+// i / n (returned) and i % n (in rem) for wave-uniform i and n from the
+// reciprocal r above, in scalar registers.
+__device__ __forceinline__ uint32_t div_by(uint32_t i, uint32_t n, uint32_t r, uint32_t& rem) {
+    uint32_t q = n == 1 ? i : __umulhi(i, r);
+    uint32_t m = i - q * n;
+    if (static_cast<int32_t>(m) < 0) {  // one too many
+        q -= 1;
+        m += n;
+    }
+    rem = m;
+    return q;
+}
 constexpr int kWeightTop = 8;  // a row's largest |scale| * 2^(8 - E_r) is below 2^8
 
 // B fragments in LDS: 1 KiB of operand (lanes 0-31 then lanes 32-63, 512
@@ -319,7 +339,8 @@ template <uint32_t WT, bool SF16>
 __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ d, const int32_t* __restrict__ rexp,
     const uint4* __restrict__ xs, const int32_t* __restrict__ tshift, float* __restrict__ out,
-    uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_n, uint32_t tiles_m, uint32_t kb_split) {
+    uint32_t M, uint32_t N, uint32_t K, uint32_t tiles_n, uint32_t tiles_m, uint32_t kb_split,
+    uint32_t inv_tiles_n, uint32_t inv_tiles_m) {
     using C = Cfg<WT, SF16>;
     constexpr int NT = C::NT, KG = C::KG, QW = C::QW, RA = C::RA, D = C::D;
     constexpr uint32_t SB = C::SB, BLK_Q = C::BLK_Q;
@@ -333,8 +354,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_kernel(
     // run of tile indexes L = (split * tiles_m + tile_m) * tiles_n + tile_n
     const uint32_t nwg = gridDim.x, id = blockIdx.x;
     const uint32_t L = (nwg & 7) == 0 ? (id & 7) * (nwg >> 3) + (id >> 3) : id;
-    const uint32_t tile_n = L % tiles_n, g = L / tiles_n;
-    const uint32_t tile_m = g % tiles_m, split = g / tiles_m;
+    // (divisions by multiplication with the host's reciprocals, in scalar
+    // registers: a plain division runs on the vector units, and the buffer
+    // descriptors derived from its result would then be used through a loop
+    // over their distinct values at every load)
+    uint32_t tile_n, tile_m;
+    const uint32_t g = div_by(L, tiles_n, inv_tiles_n, tile_n);
+    const uint32_t split = div_by(g, tiles_m, inv_tiles_m, tile_m);
     const uint32_t n0 = tile_n * C::BN, m0 = tile_m * C::BM;
     const uint32_t KB = K / 32;
     const uint32_t kb0 = split * kb_split;
@@ -633,7 +659,8 @@ hipError_t launch_mm(const MatView& m, const uint4* xs, const int32_t* tsh, floa
     if (nwg > 0x7FFFFFFFull) return hipErrorInvalidValue;
     hipLaunchKernelGGL((mm::gemm_f16_kernel<WT, SF16>), dim3(static_cast<uint32_t>(nwg)),
                        dim3(mm::kThreads), 0, s, m.q, m.d, m.rexp, xs, tsh, out, M, m.rows, m.cols,
-                       p.tiles_n, p.tiles_m, p.kb_split);
+                       p.tiles_n, p.tiles_m, p.kb_split, mm::reciprocal(p.tiles_n),
+                       mm::reciprocal(p.tiles_m));
     return hipGetLastError();
 }
 
