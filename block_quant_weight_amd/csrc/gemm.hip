@@ -246,18 +246,19 @@ constexpr int kWeightTop = 8;  // a row's largest |scale| * 2^(8 - E_r) is below
 
 // B fragments in LDS: 1 KiB of operand (lanes 0-31 then lanes 32-63, 512
 // bytes each, with 64 bytes between the halves), fragments 1280 bytes apart,
-// and the fragments of block b of a step shifted by b * 128 bytes.  A wave's
-// 16-byte fragment read stays 256 contiguous bytes per 16 lanes, and the
-// decode's writes (16 lanes: 4 rows x the 4 half blocks of a row) fall on
-// 16 different 16-byte bank groups.
+// and fragment f = (2 b + s) * 4 + j (block b of a step, k slice s, row
+// tile j) shifted by 32 b + 64 s bytes.  A wave's 16-byte fragment read
+// stays 256 contiguous bytes per 16 lanes (a read's 16-lane phase over the
+// 64 banks), and the decode's 16-byte writes fall on 8 different 16-byte
+// groups of each 128 bytes per 8 consecutive lanes (a write's phase).
 constexpr uint32_t kFragStride = 1280;
 constexpr uint32_t frag_off(uint32_t b, uint32_t f, uint32_t slot) {
-    return f * kFragStride + b * 128 + (slot >> 5) * 64 + slot * 16;
+    return f * kFragStride + b * 32 + ((f >> 2) & 1) * 64 + (slot >> 5) * 64 + slot * 16;
 }
 
 template <uint32_t WT, bool SF16>
 struct Cfg {
-    static constexpr int NT = 4;                          // 32-row tiles per workgroup
+    static constexpr int NT = 4;                          // 32-row tiles per workgroup (frag_off assumes 4)
     static constexpr int KG = 2;                          // blocks per step = k groups of waves
     static constexpr int WM = 4;                          // token waves of 64 per k group
     static constexpr int BM = 64 * WM;                    // tokens per tile
