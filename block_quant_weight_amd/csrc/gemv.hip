@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
 // Work split: one wavefront owns NR consecutive rows; lane l reads the 16-byte
 // chunks l, l + 64, ... of each row (a Q4_0 chunk is a whole block, a Q8_0
 // chunk half a block).  Order of requests at entry:
-//   1. the thread's share of the activations (16 values per half block),
+//   1. the thread's share of the activations (a half or a quarter block),
 //   2. every scale, then every quant chunk of the wave's rows (raw buffer
 //      loads; a step past the row's end gets an out-of-range offset: zeros,
 //      no traffic, and no branch around the load),
@@ -416,6 +416,95 @@ __device__ __forceinline__ bool stage_half(const float4 (&xv)[4], uint32_t h,
     return small != 0;
 }
 
+// Reductions over the 8 lanes of an aligned group (xor 1, xor 2 by quad
+// permutes, then the other quad of the eight by row_half_mirror).
+__device__ __forceinline__ uint32_t group8_max(uint32_t v) {
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
+    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true)));
+    return max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, true)));
+}
+__device__ __forceinline__ uint32_t group8_or(uint32_t v) {
+    v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true));
+    v |= static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true));
+    return v | static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x141, 0xF, 0xF, true));
+}
+__device__ __forceinline__ int group8_add(int v) {
+    v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
+    v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);
+    return v + __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);
+}
+
+// Converts quarter block q (4 activations xv) and stores its digits and,
+// from the block's first lane (first two for Q8_0), the block info.  The
+// eight quarters of a block sit in an aligned group of 8 lanes of one wave,
+// which exchange the block's largest magnitude, digit sums and mask.  `dig`
+// and `info` point at the vector's LDS area; q is the quarter's index
+// within its vector.  Returns true if the quarter holds a small value
+// (below).
+template <uint32_t WT>
+__device__ __forceinline__ bool stage_quarter(const float4 xv, uint32_t q, int4* __restrict__ dig,
+                                              void* __restrict__ info) {
+    using L = DigitLayout<WT>;
+    const float v[4] = {xv.x, xv.y, xv.z, xv.w};
+    // largest magnitude as an integer maximum of the absolute bit patterns,
+    // so that inf and NaN win over every finite value
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu);
+    m = group8_max(m);
+    const int E = __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, m));
+    const float sx = m >= 0x7F800000u ? __builtin_bit_cast(float, 0x7FC00000u)
+                                      : __builtin_amdgcn_ldexpf(1.0f, E - 30);
+    // X = rne(x * 2^(30-E)) (exact scaling, then a round to integer), biased
+    // by 128 in each of its four bytes.  A nonzero value whose X is below
+    // 2^9 in magnitude would keep less than 10 significant bits: such a
+    // ("small") value is left out of the digits (X = 0 there), marked in the
+    // chunk's mask, and its product added in float32 from the activation
+    // itself after the digit sums.
+    uint32_t u[4];
+    uint32_t small = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int X = static_cast<int>(__builtin_rintf(__builtin_amdgcn_ldexpf(v[i], 30 - E)));
+        const bool sm = static_cast<uint32_t>(X + 511) < 1023u &&
+                        (__builtin_bit_cast(uint32_t, v[i]) << 1) != 0u;
+        small |= sm ? (1u << i) : 0u;
+        u[i] = sm ? 0x80808080u : static_cast<uint32_t>(X) + 0x80808080u;
+    }
+    uint32_t pl[4];
+    transpose4(u[0], u[1], u[2], u[3], pl);
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) pl[dd] ^= 0x80808080u;  // byte + 128 -> signed digit
+    // quarter e of block blk: elements 4e .. 4e + 3 of the block, word e % 4
+    // of half (Q4_0) or chunk (Q8_0) e / 4; the block's mask has element i
+    // at bit i
+    const uint32_t e = q & 7, blk = q >> 3;
+    const uint32_t mask = group8_or(small << (4 * e));
+    if constexpr (WT == kQ4) {
+        const uint32_t k = blk >> 6, l = blk & 63, half = e >> 2;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+            reinterpret_cast<uint32_t*>(dig + (k * L::P + 2 * dd + half) * 64 + l)[e & 3] = pl[dd];
+        int sd[4];
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) sd[dd] = group8_add(__builtin_amdgcn_sdot4(pl[dd], 0x01010101, 0, false));
+        // the -8 offset's exact starting values of planes 0 + 1 and 2 + 3
+        if (e == 0)
+            static_cast<int4*>(info)[k * 64 + l] =
+                make_int4(-8 * (sd[0] + 256 * sd[1]), -8 * (sd[2] + 256 * sd[3]),
+                          __builtin_bit_cast(int, sx), static_cast<int>(mask));
+    } else {
+        const uint32_t c = 2 * blk + (e >> 2), k = c >> 6, l = c & 63;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+            reinterpret_cast<uint32_t*>(dig + (k * L::P + dd) * 64 + l)[e & 3] = pl[dd];
+        if ((e & 3) == 0)
+            static_cast<uint2*>(info)[k * 64 + l] =
+                make_uint2(__builtin_bit_cast(uint32_t, sx), (e >> 2) ? mask >> 16 : mask & 0xFFFFu);
+    }
+    return small != 0;
+}
+
 // The small-value mask of chunk slot `is` of a vector's block info.
 template <uint32_t WT>
 __device__ __forceinline__ uint32_t chunk_mask(const uint8_t* __restrict__ info, uint32_t is) {
@@ -551,13 +640,23 @@ __device__ __forceinline__ void chunk_rows(const uint4 (&qv)[NR][SMAX], const ui
     }
 }
 
-// Half blocks of activations each thread loads before the quants: enough for
+// Activations per staging thread: a half block (16) when the vectors have
+// at least 256 half blocks (a wave's worth for each SIMD), else a quarter
+// block (4), so that short vectors are converted by all four SIMDs (the
+// quarter form takes more instructions per value).
+template <uint32_t WT, int NB, int SMAX>
+constexpr int stage_values() {
+    return NB * SMAX * 64 * DigitLayout<WT>::CW / 16 >= 256 ? 16 : 4;
+}
+
+// Staging parts each thread loads before the quants: enough for
 // NB vectors of up to SMAX steps (at most 2; any rest is loaded afterwards).
 template <uint32_t WT, int NB, int SMAX, int WAVES>
 constexpr int stage_rounds() {
-    constexpr int halves = NB * SMAX * 64 * DigitLayout<WT>::CW / 16;
-    constexpr int r = (halves + WAVES * 64 - 1) / (WAVES * 64);
-    return r < 1 ? 1 : (r > 2 ? 2 : r);
+    constexpr int parts = NB * SMAX * 64 * DigitLayout<WT>::CW / stage_values<WT, NB, SMAX>();
+    constexpr int r = (parts + WAVES * 64 - 1) / (WAVES * 64);
+    constexpr int rmax = stage_values<WT, NB, SMAX>() == 4 ? 4 : 2;
+    return r < 1 ? 1 : (r > rmax ? rmax : r);
 }
 
 // The one-shot product of workgroup `block` (blockIdx.x of a plain launch,
@@ -579,21 +678,22 @@ __device__ __forceinline__ void oneshot_body(
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t nchunks = cols / CW;
     const uint32_t S = (nchunks + 63) / 64;     // <= SMAX (host-checked)
-    const uint32_t nhalf = cols / 16;           // half blocks per vector
-    const uint32_t nstage = NB * nhalf;
+    constexpr int SV = stage_values<WT, NB, SMAX>();  // activations per staging part
+    const uint32_t nparts = cols / SV;          // staging parts per vector
+    const uint32_t nstage = NB * nparts;
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const uint32_t dig_bytes = S * P * 64 * 16;     // per vector
     const uint32_t vec_bytes = L::vector_bytes(S);  // digits + info, per vector
 
     // ---- 1. this thread's activations ----
     const float4* x4 = reinterpret_cast<const float4*>(x);
-    float4 xr[XR][4];
+    float4 xr[XR][SV / 4];
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
         const uint32_t j = tid + i * THREADS;
         if (j < nstage) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) xr[i][g] = x4[4ull * j + g];
+            for (int g = 0; g < SV / 4; ++g) xr[i][g] = x4[(SV / 4) * j + g];
         }
     }
 
@@ -636,10 +736,16 @@ __device__ __forceinline__ void oneshot_body(
 
     // ---- 3. activations -> digits in LDS ----
     bool mysmall = false;
-    auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
-        const uint32_t b = j / nhalf, h = j - b * nhalf;
+    // (a block's two halves, or eight quarters, are aligned adjacent lanes:
+    // THREADS and the parts per vector are multiples of 8, and all of a
+    // block's parts are staged or none)
+    auto stage = [&](uint32_t j, const float4 (&xv)[SV / 4]) {
+        const uint32_t b = j / nparts, pi = j - b * nparts;
         uint8_t* base = lds + b * vec_bytes;
-        mysmall |= stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
+        if constexpr (SV == 16)
+            mysmall |= stage_half<WT>(xv, pi, reinterpret_cast<int4*>(base), base + dig_bytes);
+        else
+            mysmall |= stage_quarter<WT>(xv[0], pi, reinterpret_cast<int4*>(base), base + dig_bytes);
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -647,9 +753,9 @@ __device__ __forceinline__ void oneshot_body(
         if (j < nstage) stage(j, xr[i]);
     }
     for (uint32_t j = tid + XR * THREADS; j < nstage; j += THREADS) {
-        float4 xv[4];
+        float4 xv[SV / 4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) xv[g] = x4[4ull * j + g];
+        for (int g = 0; g < SV / 4; ++g) xv[g] = x4[(SV / 4) * j + g];
         stage(j, xv);
     }
     __shared__ uint32_t small_slots[WAVES];
@@ -961,8 +1067,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     const uint32_t lane = tid & 63;
     const uint32_t wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t S = (cols / L::CW + 63) / 64;
-    const uint32_t nhalf = cols / 16;
-    const uint32_t nstage = NB * nhalf;
+    constexpr int SV = stage_values<WT, NB, SMAX>();
+    const uint32_t nparts = cols / SV;
+    const uint32_t nstage = NB * nparts;
     uint8_t* lds = reinterpret_cast<uint8_t*>(smem);
     const uint32_t dig_bytes = S * L::P * 64 * 16;
     const uint32_t vec_bytes = L::vector_bytes(S);
@@ -983,13 +1090,13 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
 
     // activations first, then the first tiles
     const float4* x4 = reinterpret_cast<const float4*>(x);
-    float4 xr[XR][4];
+    float4 xr[XR][SV / 4];
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
         const uint32_t j = tid + i * THREADS;
         if (j < nstage) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) xr[i][c] = x4[4ull * j + c];
+            for (int g = 0; g < SV / 4; ++g) xr[i][g] = x4[(SV / 4) * j + g];
         }
     }
     uint32_t mat = 0;
@@ -1003,10 +1110,13 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     load_any(tile(t), ra);
 
     bool mysmall = false;
-    auto stage = [&](uint32_t j, const float4 (&xv)[4]) {
-        const uint32_t v = j / nhalf, h = j - v * nhalf;
+    auto stage = [&](uint32_t j, const float4 (&xv)[SV / 4]) {
+        const uint32_t v = j / nparts, pi = j - v * nparts;
         uint8_t* base = lds + v * vec_bytes;
-        mysmall |= stage_half<WT>(xv, h, reinterpret_cast<int4*>(base), base + dig_bytes);
+        if constexpr (SV == 16)
+            mysmall |= stage_half<WT>(xv, pi, reinterpret_cast<int4*>(base), base + dig_bytes);
+        else
+            mysmall |= stage_quarter<WT>(xv[0], pi, reinterpret_cast<int4*>(base), base + dig_bytes);
     };
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
@@ -1014,9 +1124,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
         if (j < nstage) stage(j, xr[i]);
     }
     for (uint32_t j = tid + XR * THREADS; j < nstage; j += THREADS) {
-        float4 xv[4];
+        float4 xv[SV / 4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) xv[c] = x4[4ull * j + c];
+        for (int g = 0; g < SV / 4; ++g) xv[g] = x4[(SV / 4) * j + g];
         stage(j, xv);
     }
     __shared__ uint32_t small_slots[kStreamWaves];
