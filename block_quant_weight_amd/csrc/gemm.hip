@@ -83,30 +83,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Activation staging: one workgroup of 256 threads per token (and one per
-// padding token up to a multiple of 32, which writes zeros).  Each thread
-// holds up to 8 pieces of 8 values; all of them are requested before any is
-// used, so a token costs one round trip to memory (rows of more than 16384
-// values are taken in chunks, read twice).
+// Activation staging: one workgroup per kStageTokens consecutive tokens of a
+// 32-token tile (padding tokens up to a multiple of 32 write zeros).  Lane
+// kStageTokens * j + m of a wave holds token m's pieces (8 values each), so
+// that a load reads 64 / kStageTokens consecutive pieces of each token's row
+// and a store writes kStageTokens consecutive 16-byte slots of one fragment
+// line (the slots of the tile's tokens for one piece are adjacent).  Every
+// piece of a chunk is requested before any is used, so a token costs one
+// round trip to memory (rows longer than a chunk are read twice).
 // ---------------------------------------------------------------------------
 
-constexpr int kTokenTop = 14;    // a token's largest staged magnitude is in [2^13, 2^14)
-constexpr int kStagePieces = 8;  // pieces per thread per chunk
+constexpr int kTokenTop = 14;     // a token's largest staged magnitude is in [2^13, 2^14)
 constexpr int kTokensPerTile = 32;
+constexpr int kStageTokens = 2;   // tokens per workgroup (divides 32; 4 and 8 measured slower: fewer workgroups)
+constexpr int kStageThreads = 256 * (kStageTokens > 2 ? kStageTokens / 2 : 1);
+template <bool XF32>
+constexpr int stage_pieces() { return XF32 ? 8 : 16; }  // pieces per thread per chunk
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, true)));
-    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, true)));
-    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x124, 0xF, 0xF, true)));
-    v = max(v, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true)));
-    const uint32_t a = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0)),
-                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16)));
-    const uint32_t b = max(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32)),
-                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48)));
-    return max(a, b);
-}
-
-// Raw data of one piece (8 values): bf16 bits in r[0..3], or f32 in r[0..7].
 template <bool XF32>
 struct Piece {
     uint32_t r[XF32 ? 8 : 4];
@@ -154,65 +147,74 @@ __device__ __forceinline__ uint4 piece_f16(const Piece<XF32>& v, int sh, bool ba
 }
 
 template <bool XF32>
-__global__ __launch_bounds__(256) void stage_x_kernel(const void* __restrict__ x, uint32_t M,
-                                                      uint32_t K, uint4* __restrict__ xs,
-                                                      int32_t* __restrict__ tshift) {
-    __shared__ uint32_t red[4];
-    // token of this workgroup: workgroups go to the 8 XCDs round-robin, so
-    // contiguous runs of tokens are given to one XCD (when the padded batch
-    // allows) and each 32-token fragment is assembled in one L2, not
-    // written in 16-byte parts from eight
+__global__ __launch_bounds__(kStageThreads) void stage_x_kernel(const void* __restrict__ x, uint32_t M,
+                                                                uint32_t K, uint4* __restrict__ xs,
+                                                                int32_t* __restrict__ tshift) {
+    constexpr int T = kStageTokens, J = 64 / T, W = kStageThreads / 64, NP = stage_pieces<XF32>();
+    constexpr uint32_t LANES = kStageThreads / T;  // lanes per token
+    constexpr uint32_t CH = LANES * NP;            // pieces per token per chunk
+    __shared__ uint32_t red[W * T];
+    // token group of this workgroup: workgroups go to the 8 XCDs
+    // round-robin, so contiguous runs of groups are given to one XCD (when
+    // the padded batch allows) and each 32-token fragment is assembled in
+    // one L2, not written in parts from eight
     const uint32_t nwg = gridDim.x, id = blockIdx.x;
-    const uint32_t t = (nwg % (8 * kTokensPerTile)) == 0 ? (id & 7) * (nwg >> 3) + (id >> 3) : id;
-    const int tid = threadIdx.x;
+    const uint32_t grp = (nwg % (8 * (kTokensPerTile / T))) == 0 ? (id & 7) * (nwg >> 3) + (id >> 3) : id;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t m = lane % T, j = lane / T;
+    const uint32_t t = grp * T + m;
+    const bool real = t < M;
     const uint32_t npiece = K / 8, KB = K / 32;
-    const uint32_t mt = t / kTokensPerTile, m = t % kTokensPerTile;
+    const uint32_t mt = t / kTokensPerTile, mm = t % kTokensPerTile;
     // piece p (block p / 4, group g = p % 4: slice g / 2, half g % 2) goes to
-    // fragment (mt, p / 4, g / 2), slot 32 (g % 2) + m
-    uint4* const dst = xs + static_cast<uint64_t>(mt) * KB * 128 + m;
+    // fragment (mt, p / 4, g / 2), slot 32 (g % 2) + mm
+    uint4* const dst = xs + static_cast<uint64_t>(mt) * KB * 128 + mm;
     auto slot = [&](uint32_t p) { return (p >> 2) * 128 + ((p >> 1) & 1) * 64 + (p & 1) * 32; };
-    constexpr uint32_t CH = 256 * kStagePieces;  // pieces per chunk
-    if (t >= M) {
-        for (uint32_t p = tid; p < npiece; p += 256) dst[slot(p)] = make_uint4(0, 0, 0, 0);
-        if (tid == 0) tshift[t] = 0;
-        return;
-    }
-    const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<uint64_t>(t) * K * (XF32 ? 4 : 2);
+    // this lane's pieces of a chunk: c0 + w J + j + LANES i
+    const uint32_t p_lane = w * J + j;
+    const uint8_t* xr = static_cast<const uint8_t*>(x) + static_cast<uint64_t>(real ? t : 0) * K * (XF32 ? 4 : 2);
     // largest magnitude as an integer maximum of the magnitude bits, so that
     // inf and NaN win over every finite value
-    Piece<XF32> v[kStagePieces];
+    Piece<XF32> v[NP];
     uint32_t mx = 0;
     for (uint32_t c0 = 0; c0 < npiece; c0 += CH) {
 #pragma unroll
-        for (int i = 0; i < kStagePieces; ++i) {
-            const uint32_t p = c0 + tid + 256 * i;
-            v[i] = load_piece<XF32>(xr, p, p < npiece);
+        for (int i = 0; i < NP; ++i) {
+            const uint32_t p = c0 + p_lane + LANES * i;
+            v[i] = load_piece<XF32>(xr, p, real && p < npiece);
         }
 #pragma unroll
-        for (int i = 0; i < kStagePieces; ++i) mx = max(mx, piece_max<XF32>(v[i]));
+        for (int i = 0; i < NP; ++i) mx = max(mx, piece_max<XF32>(v[i]));
     }
-    mx = wave_max_u32(mx);
-    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    // over the lanes of the same token (lane bits above those of m), then
+    // over the waves
+#pragma unroll
+    for (int d = T; d < 64; d *= 2)
+        mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), d)));
+    if (j == 0) red[w * T + m] = mx;
     __syncthreads();
-    mx = max(max(red[0], red[1]), max(red[2], red[3]));
+    mx = 0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) mx = max(mx, red[k * T + m]);
     const bool bad = mx >= 0x7F800000u;
     const int sh = (bad || mx == 0) ? 0 : kTokenTop - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mx));
     // the last chunk is still in registers; earlier ones are read again
     const uint32_t last = npiece == 0 ? 0 : (npiece - 1) / CH * CH;
     for (uint32_t c0 = 0; c0 < last; c0 += CH) {
 #pragma unroll
-        for (int i = 0; i < kStagePieces; ++i) {
-            const uint32_t p = c0 + tid + 256 * i;
-            const Piece<XF32> w = load_piece<XF32>(xr, p, p < npiece);
-            if (p < npiece) dst[slot(p)] = piece_f16<XF32>(w, sh, bad);
+        for (int i = 0; i < NP; ++i) {
+            const uint32_t p = c0 + p_lane + LANES * i;
+            const Piece<XF32> u = load_piece<XF32>(xr, p, real && p < npiece);
+            if (p < npiece) dst[slot(p)] = piece_f16<XF32>(u, sh, bad);
         }
     }
 #pragma unroll
-    for (int i = 0; i < kStagePieces; ++i) {
-        const uint32_t p = last + tid + 256 * i;
+    for (int i = 0; i < NP; ++i) {
+        const uint32_t p = last + p_lane + LANES * i;
         if (p < npiece) dst[slot(p)] = piece_f16<XF32>(v[i], sh, bad);
     }
-    if (tid == 0) tshift[t] = sh;
+    if (w == 0 && j == 0) tshift[t] = sh;
 }
 
 // ---------------------------------------------------------------------------
@@ -719,12 +721,11 @@ hipError_t launch_gemm(const MatView& m, const void* x, bool x_f32, float* y, ui
         const uint8_t* xp = static_cast<const uint8_t*>(x) + uint64_t{done} * m.cols * (x_f32 ? 4 : 2);
         float* yp = y + uint64_t{done} * m.rows;
         if (mp > 0x7FFFFFFFull) return hipErrorInvalidValue;
+        const dim3 sg(static_cast<uint32_t>(mp / kStageTokens));
         if (x_f32)
-            hipLaunchKernelGGL(stage_x_kernel<true>, dim3(static_cast<uint32_t>(mp)), dim3(256), 0, s,
-                               xp, M, m.cols, xs, tsh);
+            hipLaunchKernelGGL(stage_x_kernel<true>, sg, dim3(kStageThreads), 0, s, xp, M, m.cols, xs, tsh);
         else
-            hipLaunchKernelGGL(stage_x_kernel<false>, dim3(static_cast<uint32_t>(mp)), dim3(256), 0, s,
-                               xp, M, m.cols, xs, tsh);
+            hipLaunchKernelGGL(stage_x_kernel<false>, sg, dim3(kStageThreads), 0, s, xp, M, m.cols, xs, tsh);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         float* out = p.splits > 1 ? part : yp;
