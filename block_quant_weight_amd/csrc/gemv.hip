@@ -1325,11 +1325,13 @@ hipError_t stream_pass(const MatView* ms, uint32_t n, const float* x, float* con
 // eight) and for fewer than 4096 rows of two to four steps (1024 x 4096:
 // 2.49 -> 2.39 us), eight for other rows of up to four steps, sixteen for
 // rows of more than four steps (fewer copies of a wide vector) and for 4096
-// to 8192 rows of two to four steps, which then take one row per wave.  Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192
-// 6.1 -> 5.6 us, Q8_0 4096 x 4096 4.77 -> 4.69 us; but 11008 x 4096 Q4_0
-// 7.0 us against 6.6 us with two rows per wave in eight-wave groups, 1024 x
-// 4096 slower too, and one-step rows slower in sixteen-wave groups.
-// QMV_GEMV_NR overrides NR (tuning sweeps).
+// to 8192 rows of two to four steps, which then take one row per wave.
+// Measured: Q4_0 4096 x 4096 3.77 -> 3.62 us, Q4_0 4096 x 8192 6.1 -> 5.6
+// us, Q8_0 4096 x 4096 4.77 -> 4.69 us; but 11008 x 4096 Q4_0 7.0 us against
+// 6.6 us with two rows per wave in eight-wave groups, 1024 x 4096 slower too,
+// and one-step rows slower in sixteen-wave groups.  For Q8_0 4096 x 11008
+// (eleven steps), eight-wave groups (12.2 against 11.3 us) and two rows per
+// wave (11.8 us) were slower.
 template <uint32_t WT, bool SF16, int NB>
 hipError_t gemv_pass(const MatView& m, const float* x, float* y, hipStream_t s) {
     constexpr uint32_t CW = DigitLayout<WT>::CW;
