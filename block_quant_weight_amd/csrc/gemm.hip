@@ -48,9 +48,10 @@
 // 16 h .. 16 h + 15) holds g = 2 h and 2 h + 1.  Four consecutive threads
 // take one row's two blocks of a step, so that a wave's quant load covers
 // 16 rows x 32 (or 64) contiguous bytes, the pattern the address units
-// serve fastest.  Each step first requests its activations two steps ahead
+// serve fastest.  Each step first requests its activations one step ahead
 // and then its weights three steps ahead (loads complete in order, so the
-// activations never wait behind a weight load of the same step); all loads
+// activations never wait behind a weight load of the same step; a second
+// step of activations in flight measured slower); all loads
 // are raw buffer loads, with an out-of-range offset (zeros, no traffic)
 // past any edge.  At the end the two k groups exchange half of their sums
 // through LDS, and each wave scales and stores two of the four row tiles
@@ -276,7 +277,7 @@ struct Cfg {
     static constexpr int TSH = RED;
     static constexpr int LDS = 2 * STAGE > RED + BM * 4 ? 2 * STAGE : RED + BM * 4;
     static_assert(KG == 2, "two k groups share the output tiles");
-    static constexpr int RA = 3;                          // A register sets (two steps ahead)
+    static constexpr int RA = 2;                          // A register sets (one step ahead)
     static constexpr int D = 3;                           // weight register sets (D steps ahead)
     static constexpr int UNROLL = 6;
     static_assert(UNROLL % RA == 0 && UNROLL % D == 0 && UNROLL % 2 == 0, "");
