@@ -31,8 +31,9 @@ per matrix), writer_q4_14336x4096 (float32 weights to a Q4_0 f16-scale image
 by the round rule), writer_q4_search_14336x4096 (the least-squares search,
 bound by float32 arithmetic), gemm_q8act_q4_14336x4096 and
 gemm_q8act_q8_4096x14336 (the prefill shapes on the int8 path), read_stream
-(the read ceiling over a range of sizes), and copy (a plain device copy, used
-to calibrate HBM byte counters).
+(the read ceiling over a range of sizes), mfma_rate (the prefill product's
+matrix-core instruction back to back, on constant and on random operands),
+and copy (a plain device copy, used to calibrate HBM byte counters).
 """
 from __future__ import annotations
 
@@ -122,6 +123,8 @@ def workload(name):
         return ("plain device copy of 256 MiB (counter calibration)", "copy", 0, [], 0)
     if name == "read_stream":
         return ("read ceiling: qmv_read_probe over a range of sizes", "read", 0, [], 0)
+    if name == "mfma_rate":
+        return ("matrix-core rate: qmv_mfma_probe, v_mfma_f32_32x32x16_f16 back to back", "mfma", 0, [], 0)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -355,6 +358,8 @@ def measure(name, args, stream, cpu_budget):
         return run_writer(args, name, desc, config, mats, stream, cpu_budget)
     if kind == "read":
         return read_stream(args, stream)
+    if kind == "mfma":
+        return mfma_rate(args, stream)
 
     groups = launch_groups(name, mats)
     gated = name == "decode_layer_gated"
@@ -676,6 +681,49 @@ def read_stream(args, stream):
     return {"metric": "read ceiling GB/s (qmv_read_probe)", "value": best["GB/s"], "unit": "GB/s",
             "n_gpus": 1, "higher_is_better": True, "config": {"workload": "read_stream"},
             "ceilings": res}
+
+
+MFMA_FLOPS = 32 * 32 * 16 * 2  # one v_mfma_f32_32x32x16_f16
+
+
+def mfma_rate(args, stream, iters=4096, reps=5):
+    """Back-to-back rate of the prefill product's matrix-core instruction
+    (qmv_mfma_probe) at one and two waves per SIMD, on constant and on
+    pseudo-random operands: TFLOP/s from the launches' HIP-event time, the
+    cycles per product and the clock from the waves' own counters."""
+    import torch
+    from block_quant_weight_amd import qmv as Q
+    res = []
+    for wps in (1, 2):
+        waves = 1024 * wps
+        clocks = torch.zeros(2 * waves, dtype=torch.int64, device="cuda")
+        sink = torch.zeros(64 * waves, dtype=torch.float32, device="cuda")
+        for rnd in (0, 1):
+            for _ in range(2):
+                Q.qmv_mfma_probe(rnd, wps, iters, clocks, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                Q.qmv_mfma_probe(rnd, wps, iters, clocks, sink)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            c = clocks.view(-1, 2).double().cpu()
+            cyc, ticks = c[:, 0].mean().item(), c[:, 1].mean().item()
+            products = 8 * iters
+            r = {"waves_per_simd": wps, "operands": "random" if rnd else "constant",
+                 "us_per_launch": round(ms * 1e3, 2),
+                 "TFLOP/s": round(MFMA_FLOPS * products * waves / (ms * 1e-3) / 1e12, 1),
+                 "frac_of_peak": round(MFMA_FLOPS * products * waves / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "cycles_per_product_per_wave": round(cyc / products, 2),
+                 "clock_GHz": round(cyc / (ticks / 100e6) / 1e9, 3)}
+            res.append(r)
+            log(f"mfma rate, {wps} wave(s) per SIMD, {r['operands']} operands: {r['TFLOP/s']:.0f} TFLOP/s, "
+                f"{r['cycles_per_product_per_wave']:.1f} cycles per product per wave, clock {r['clock_GHz']:.2f} GHz")
+    best = max((r for r in res if r["operands"] == "random"), key=lambda r: r["TFLOP/s"])
+    return {"metric": "matrix-core rate TFLOP/s (qmv_mfma_probe, random operands)", "value": best["TFLOP/s"],
+            "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True, "config": {"workload": "mfma_rate"},
+            "rates": res}
 
 
 def gemv_launch_bytes(name):

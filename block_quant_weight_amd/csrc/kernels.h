@@ -106,5 +106,9 @@ hipError_t launch_block_dots(const MatView& m, const int8_t* xq, int32_t* s,
 
 // Reads n16 16-byte words from src (measurement aid: the read ceiling).
 hipError_t launch_read_probe(const void* src, uint64_t n16, uint32_t* sink, hipStream_t stream);
+// One workgroup per compute unit (256), 4 or 8 waves (1 or 2 per SIMD).
+constexpr uint32_t kProbeWorkgroups = 256;
+hipError_t launch_mfma_probe(bool random, uint32_t waves_per_simd, uint32_t iters, uint64_t* clocks,
+                             float* sink, hipStream_t stream);
 
 }  // namespace qmv

@@ -13,6 +13,15 @@
 // case that the fold equals a fixed constant, which keeps the loads without
 // a store stream.
 //
+// Matrix-core rate probe (a measurement aid, no part of the product): every
+// wave runs eight independent chains of v_mfma_f32_32x32x16_f16, the
+// prefill product's instruction, and records the shader-clock cycles and
+// the 100 MHz wall-clock ticks its chains took; operands are either
+// constant (1 and 0) or two sets of hashed values in [-0.5, 0.5) that
+// alternate from one product to the next, as the operands of a real
+// product change, since the clock the power limit allows depends on how
+// many bits the matrix cores' inputs toggle.
+//
 // Quantizer: the page's "Quantization rule" in separate float32 operations
 // (__fmul_rn / __fadd_rn cannot be fused; float division is correctly
 // rounded on this target).
@@ -193,6 +202,67 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint8_t* __restri
     if (acc == kProbeMagic) sink[blockIdx.x & 63] = acc;
 }
 
+constexpr uint32_t kMfmaChains = 8;
+
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    return x ^ (x >> 16);
+}
+
+// Wave w of the grid writes clocks[2 w] (shader-clock cycles) and
+// clocks[2 w + 1] (100 MHz ticks) over its iters x kMfmaChains products,
+// and its lanes' sums to sink[64 w + lane] (which keeps the products).
+template <bool RANDOM>
+__global__ __launch_bounds__(512) void mfma_probe_kernel(uint64_t* __restrict__ clocks, uint32_t iters,
+                                                         float* __restrict__ sink) {
+    typedef _Float16 probe_f16x8 __attribute__((ext_vector_type(8)));
+    typedef float probe_f32x16 __attribute__((ext_vector_type(16)));
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t gw = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    probe_f16x8 a[2], b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (RANDOM) {
+                a[j][i] = static_cast<_Float16>(
+                    static_cast<float>(probe_hash(lane * 131u + i + gw * 7u + j * 5003u) & 0xFFFFu) / 65536.0f - 0.5f);
+                b[j][i] = static_cast<_Float16>(
+                    static_cast<float>(probe_hash(lane * 977u + i * 13u + gw + j * 7919u) & 0xFFFFu) / 65536.0f - 0.5f);
+            } else {
+                a[j][i] = static_cast<_Float16>(1.0f);
+                b[j][i] = static_cast<_Float16>(0.0f);
+            }
+        }
+    probe_f32x16 acc[kMfmaChains];
+#pragma unroll
+    for (uint32_t k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t w0 = __builtin_amdgcn_s_memrealtime();
+    for (uint32_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (uint32_t k = 0; k < kMfmaChains; ++k)
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k & 1], b[k & 1], acc[k], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (uint32_t k = 0; k < kMfmaChains; ++k)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += acc[k][v];
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t w1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+        clocks[2 * gw] = t1 - t0;
+        clocks[2 * gw + 1] = w1 - w0;
+    }
+    sink[gw * 64 + lane] = sum;
+}
+
 }  // namespace
 
 hipError_t launch_embed(const MatView& m, const int32_t* ids, uint32_t n,
@@ -242,6 +312,16 @@ hipError_t launch_read_probe(const void* src, uint64_t n16, uint32_t* sink, hipS
     if (grid > 0x7FFFFFFFull) return hipErrorInvalidValue;
     hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
                        static_cast<const uint8_t*>(src), nbytes, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(bool random, uint32_t waves_per_simd, uint32_t iters, uint64_t* clocks,
+                             float* sink, hipStream_t s) {
+    const dim3 grid(kProbeWorkgroups), block(256 * waves_per_simd);
+    if (random)
+        hipLaunchKernelGGL(mfma_probe_kernel<true>, grid, block, 0, s, clocks, iters, sink);
+    else
+        hipLaunchKernelGGL(mfma_probe_kernel<false>, grid, block, 0, s, clocks, iters, sink);
     return hipGetLastError();
 }
 

@@ -398,4 +398,15 @@ int qmv_read_probe(const void* src, uint64_t nbytes, uint32_t* sink, void* strea
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int qmv_mfma_probe(uint32_t random_operands, uint32_t waves_per_simd, uint32_t iters, uint64_t* clocks,
+                   float* sink, void* stream) {
+    clear_stale_error();
+    if (clocks == nullptr || sink == nullptr || random_operands > 1) return QMV_E_ARG;
+    if (waves_per_simd < 1 || waves_per_simd > 2 || iters < 1 || iters > (1u << 20)) return QMV_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(clocks) & 7u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return QMV_E_ARG;
+    return device_status(qmv::launch_mfma_probe(random_operands != 0, waves_per_simd, iters, clocks, sink,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

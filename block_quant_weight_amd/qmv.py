@@ -24,7 +24,7 @@ EXPORTS = ("qmv_span", "qmv_class_wtype", "qmv_create", "qmv_upload",
            "qmv_destroy", "qmv_gemv", "qmv_gemv_group", "qmv_gemm", "qmv_embed_rows",
            "qmv_quantize_q8", "qmv_block_dots", "qmv_status_str", "qmv_gguf_span",
            "qmv_upload_gguf", "qmv_quantize_weights", "qmv_gemv_gated", "qmv_gemm_q8",
-           "qmv_read_probe", "qmv_gemm_noalloc")
+           "qmv_read_probe", "qmv_gemm_noalloc", "qmv_mfma_probe")
 
 _lib = None
 
@@ -68,6 +68,7 @@ def lib():
             "qmv_gemm_q8": ([vp, vp, vp, vp, u32, vp], i32),
             "qmv_read_probe": ([vp, u64, vp, vp], i32),
             "qmv_gemm_noalloc": ([vp, vp, vp, u32, vp], i32),
+            "qmv_mfma_probe": ([u32, u32, u32, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -326,3 +327,17 @@ def qmv_read_probe(src, nbytes, sink, stream=None):
         raise QmvError(QMV_E_ARG, "qmv_read_probe")
     _check(lib().qmv_read_probe(src.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)),
            "qmv_read_probe")
+
+
+def qmv_mfma_probe(random_operands, waves_per_simd, iters, clocks, sink, stream=None):
+    """Back-to-back matrix-core products (a measurement aid): clocks, int64
+    GPU tensor of 2 * 1024 * waves_per_simd elements (cycles and 100 MHz
+    ticks per wave); sink, float32 GPU tensor of 64 * 1024 * waves_per_simd."""
+    import torch
+    waves = 1024 * waves_per_simd
+    if not (clocks.is_cuda and sink.is_cuda) or clocks.dtype != torch.int64 or sink.dtype != torch.float32:
+        raise QmvError(QMV_E_ARG, "qmv_mfma_probe")
+    if clocks.numel() < 2 * waves or sink.numel() < 64 * waves:
+        raise QmvError(QMV_E_ARG, "qmv_mfma_probe")
+    _check(lib().qmv_mfma_probe(int(random_operands), int(waves_per_simd), int(iters), clocks.data_ptr(),
+                                sink.data_ptr(), _stream(stream)), "qmv_mfma_probe")

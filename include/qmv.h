@@ -366,6 +366,23 @@ int qmv_block_dots(qmv_handle h, const int8_t *xq, int32_t *s, void *stream);
  */
 int qmv_read_probe(const void *src, uint64_t nbytes, uint32_t *sink, void *stream);
 
+/*
+ * Measurement aid, not part of the product: the rate of the prefill
+ * product's matrix-core instruction (v_mfma_f32_32x32x16_f16) back to
+ * back, the ceiling against which the product's rate is set.  256
+ * workgroups of 4 * waves_per_simd waves (waves_per_simd 1 or 2); every
+ * wave runs 8 independent chains of iters products (iters 1 .. 2^20) on
+ * constant operands (random_operands 0: 1 and 0) or on two alternating sets
+ * of pseudo-random values in [-0.5, 0.5) (1), and writes clocks[2 w] =
+ * shader-clock cycles and clocks[2 w + 1] = 100 MHz wall-clock ticks of its
+ * chains (w = wave index over the grid).  clocks: 2 * 1024 * waves_per_simd
+ * uint64 of device memory, 8-byte aligned; sink: 64 * 1024 * waves_per_simd
+ * floats of device memory (the lanes' sums, which keep the products).
+ * Errors: QMV_E_ARG, QMV_E_DEVICE.
+ */
+int qmv_mfma_probe(uint32_t random_operands, uint32_t waves_per_simd, uint32_t iters,
+                   uint64_t *clocks, float *sink, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *qmv_status_str(int status);
 

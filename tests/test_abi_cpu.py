@@ -25,7 +25,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     L = Q.lib()
     declared = header_functions()
-    assert len(declared) == 19
+    assert len(declared) == 20
     assert sorted(Q.EXPORTS) == declared
     for name in declared:
         assert hasattr(L, name), name

@@ -46,3 +46,48 @@ def test_probe_rejects_bad_arguments():
     assert L.qmv_read_probe(p, 16, k + 2, s) == Q.QMV_E_ARG
     assert L.qmv_read_probe(p, 4096, k, s) == Q.QMV_OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wps,rnd", [(1, 0), (1, 1), (2, 0), (2, 1)])
+def test_mfma_probe_counts_and_writes_only_its_outputs(wps, rnd):
+    """Every wave reports a positive cycle and tick count within the range
+    the products' count allows; the lanes' sums are finite (zero for the
+    constant operands, whose second factor is 0); nothing past the outputs
+    changes."""
+    import torch
+    waves = 1024 * wps
+    iters = 64
+    clocks = torch.zeros(2 * waves + 16, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(64 * waves + 64, dtype=torch.float32, device="cuda")
+    Q.qmv_mfma_probe(rnd, wps, iters, clocks, sink)
+    torch.cuda.synchronize()
+    c = clocks[:2 * waves].view(-1, 2).cpu()
+    products = 8 * iters
+    assert bool((c[:, 0] >= 4 * products).all()) and bool((c[:, 0] < 4096 * products).all())
+    assert bool((c[:, 1] > 0).all())
+    s = sink[:64 * waves]
+    assert bool(torch.isfinite(s).all())
+    if rnd == 0:
+        assert torch.count_nonzero(s).item() == 0
+    assert torch.count_nonzero(clocks[2 * waves:]).item() == 0
+    assert torch.count_nonzero(sink[64 * waves:]).item() == 0
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    import torch
+    L = Q.lib()
+    clocks = torch.zeros(4096, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(64 * 2048, dtype=torch.float32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    c, k = clocks.data_ptr(), sink.data_ptr()
+    assert L.qmv_mfma_probe(0, 1, 16, None, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 1, 16, c, None, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(2, 1, 16, c, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 0, 16, c, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 3, 16, c, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 1, 0, c, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 1, (1 << 20) + 1, c, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 1, 16, c + 4, k, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(0, 1, 16, c, k + 2, s) == Q.QMV_E_ARG
+    assert L.qmv_mfma_probe(1, 2, 16, c, k, s) == Q.QMV_OK
+    torch.cuda.synchronize()
