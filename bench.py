@@ -763,6 +763,18 @@ def with_ceiling(rec, name, args, stream):
     roof["read_ceiling"] = out
 
 
+def with_mfma_ceiling(rec, ceiling):
+    """Adds the matrix-core instruction's own rate on random operands at two
+    waves per SIMD (the product's occupancy) to a prefill GEMM record."""
+    c = next(r for r in ceiling["rates"] if r["operands"] == "random" and r["waves_per_simd"] == 2)
+    roof = rec["roofline"]
+    roof["mfma_ceiling"] = {"TFLOP/s": c["TFLOP/s"], "clock_GHz": c["clock_GHz"],
+                            "frac_of_ceiling": round(roof["achieved"] / c["TFLOP/s"], 4),
+                            "probe": "qmv_mfma_probe, v_mfma_f32_32x32x16_f16 back to back, random operands"}
+    log(f"{rec['config']['workload']}: {roof['achieved']:.1f} TFLOP/s against the matrix cores' "
+        f"{c['TFLOP/s']:.1f} TFLOP/s on random operands")
+
+
 def summary(rec):
     wl = rec["config"]
     return {"config": wl.get("config"), "description": wl.get("description"),
@@ -809,7 +821,12 @@ def main():
         recs[name] = measure(name, args, stream, budget)
         if name in GEMV_WORKLOADS:
             with_ceiling(recs[name], name, args, stream)
+        if name.startswith("gemm_"):
+            if "mfma" not in recs:
+                recs["mfma"] = mfma_rate(args, stream)
+            with_mfma_ceiling(recs[name], recs["mfma"])
         torch.cuda.empty_cache()
+    recs.pop("mfma", None)
     head = dict(recs[HEADLINE])
     head["configs"] = {name: summary(r) for name, r in recs.items()}
     print(json.dumps(head), flush=True)
