@@ -121,6 +121,21 @@ def test_gemv_large_batch_matrix_core_path(wt, sf, batch):
         Q.qmv_destroy(h)
 
 
+# long rows on the batched fallback (f32 activations staged as scaled f16 in
+# chunks of 8192 values: several chunks, one re-read, and a K tail)
+@pytest.mark.parametrize("wt,sf,C", [(K.Q8, 0, 14336), (K.Q4, 1, 11008), (K.Q4, 0, 16416)])
+def test_gemv_large_batch_long_rows(wt, sf, C):
+    R, batch = 70, 12
+    img = K.make_image(210, C, wt, sf, R, C)
+    h = K.upload(img, wt, sf, R, C)
+    try:
+        x = K.make_x(210, batch, batch, C)
+        ref, norm = O.product(img, wt, sf, R, C, x, threads=K.THREADS)
+        close(K.gpu_gemv(h, x), ref, norm, f"gemv-fallback {wt}/{sf} {R}x{C} b{batch}")
+    finally:
+        Q.qmv_destroy(h)
+
+
 def test_gemv_unit_vectors_give_columns_exactly():
     # x = e_c: one nonzero product per row, so y is the dequantized column
     # bit for bit (the only rounding is fl32(v * d)).
