@@ -1,6 +1,7 @@
-"""The read probe (qmv_read_probe, a measurement aid): it runs over ragged
-and large sizes without touching anything but its sink, and rejects bad
-arguments."""
+"""The two measurement aids.  The read probe (qmv_read_probe) runs over
+ragged and large sizes without touching anything but its sink; the
+matrix-core probe (qmv_mfma_probe) reports plausible cycle and tick counts
+for every wave and writes only its outputs; both reject bad arguments."""
 import ctypes
 
 import pytest
